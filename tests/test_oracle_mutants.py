@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in a copy of the oracle; the pins must catch each one.
+
+This shows the pins are strong enough: a dropped term, a wrong sign, a wrong
+index or slice, a missing scale, confused log units or an off-by-one in the
+split ranges each make at least one pin fail.  Mistakes are planted only in a
+private in-memory copy of the CPU oracle.
+"""
+import importlib.util
+import os
+import types
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "mla_oracle.py")
+
+MUTANTS = {
+    "drop_rope_term": ("qn @ K[:, :D_LATENT].T + qp @ K[:, D_LATENT:].T", "qn @ K[:, :D_LATENT].T"),
+    "rope_sign": ("qn @ K[:, :D_LATENT].T + qp @ K[:, D_LATENT:].T", "qn @ K[:, :D_LATENT].T - qp @ K[:, D_LATENT:].T"),
+    "no_scale": ("return softmax_scale * (qn", "return (qn"),
+    "lse_sign": ("return m + np.log(", "return m - np.log("),
+    "wrong_value_slice": ("return weighted_values(z, lse, K[:, :D_LATENT]), lse",
+                          "return weighted_values(z, lse, K[:, D_ROPE:D_ROPE + D_LATENT]), lse"),
+    "latent_feature_order": ("(qn @ K[:, :D_LATENT].T", "(qn[:, ::-1] @ K[:, :D_LATENT].T"),
+    "page_offset": ("pool[pages, j % page_block_size, 0, :]", "pool[pages, (j + 1) % page_block_size, 0, :]"),
+    "page_index": ("[b, j // page_block_size]", "[b, (j + 1) // page_block_size]"),
+    "row_offset": ("kv_latent[b, :L, 0, :]", "kv_latent[b, 1:L + 1, 0, :]"),
+    "bf16_decode": ("astype(np.uint32) << 16", "astype(np.uint32) << 15"),
+    "combine_units": ("total * math.log(2.0)", "total"),
+    "combine_anchor": ("w = np.exp2(lses - total)", "w = np.exp2(lses - Ms)"),
+    "split_remainder": ("1 if k < rem else 0", "1 if k <= rem else 0"),
+    "partial_base": ("return o, lse / math.log(2.0)", "return o, lse"),
+    "stabiliser_shift": ("np.exp(z - m[:, None]).sum(axis=1)", "np.exp(z - m[:, None] + 1.0).sum(axis=1)"),
+    "weights_not_normalised": ("np.exp(z - lse[:, None]) @ V", "np.exp(z) @ V"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in pins.ALL_PINS:
+            try:
+                pin(mod)
+            except (AssertionError, IndexError, ValueError) as e:
+                caught.append(pin.__name__)
+                break
+    assert caught, f"mutant {name} passed every pin"

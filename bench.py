@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MLA decode path (one GPU).
+
+A step is one full decode call (planner + split kernel + combine) over one
+batch of synthetic inputs already resident in HBM.  Default workload:
+B=64, H=128, L=4096 for every sequence, fp16, contiguous cache, i.i.d. N(0,1)
+inputs, softmax_scale = 1/sqrt(576), planner-chosen splits.
+
+Prints ONE JSON line.  Throughput is TFLOPS of the algorithmic work
+2·H·(576 + 512) per valid cache row; the line also carries KV GB/s, µs per
+call, the fraction of the per-workload roofline min(8 TB/s × intensity, 2.5
+PFLOP/s dense fp16/bf16), per-kernel timing of the split kernel from HIP events
+(`roofline`), and the fp64 CPU oracle timed on a bounded sample
+(`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0     # dense fp16 / bf16
+D_QK, D_V = 576, 512
+
+METRIC = "MLA decode TFLOPS + KV GB/s (% roofline), B=64/128 h=128 d=576/512"
+
+
+def workload_figures(lens, heads: int):
+    """Algorithmic flops and bytes of one call (cache rows, Q, out, lse)."""
+    import numpy as np
+    rows = float(np.sum(np.asarray(lens, dtype=np.int64)))
+    B = len(lens)
+    flops = 2.0 * heads * (D_QK + D_V) * rows
+    kv_bytes = rows * D_QK * 2
+    total_bytes = kv_bytes + B * heads * (D_QK * 2 + D_V * 2 + 4)
+    return flops, kv_bytes, total_bytes
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the fp64 oracle on the first sequences of the workload until ~budget_s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done, t0 = 0, time.perf_counter()
+    while done < inp.batch and time.perf_counter() - t0 < budget_s:
+        oracle.mla_decode_ref(inp, batches=[done])
+        done += 1
+    el = time.perf_counter() - t0
+    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads)
+    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} heads), fp64 NumPy, "
+                      f"{el:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: B=64 L=4096 fp16)")
+    ap.add_argument("--num-split", type=int, default=0, help="0 = planner")
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the decode path has no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import deepseek_mla_decode_amd as mla
+    import mla_inputs as mi
+    from mla_inputs.torch_io import to_device
+
+    t_gen = time.perf_counter()
+    inp = mi.make_config(args.config)
+    gen_s = time.perf_counter() - t_gen
+    dev = to_device(inp, "cuda")
+    flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads)
+    # Rotate copies of the cache when one copy would fit in the 256 MiB last-level cache.
+    copies = args.copies or (1 if kv_bytes > 1.5 * 2**30 else 3)
+    devs = [dev]
+    for _ in range(copies - 1):
+        d2 = dict(dev)
+        if inp.paged:
+            pool = dev["pool"].clone()
+            d2.update(pool=pool, kv_latent=pool[..., :512], k_pe=pool[..., 512:])
+        else:
+            d2.update(kv_latent=dev["kv_latent"].clone(), k_pe=dev["k_pe"].clone())
+        d2["q_nope"], d2["q_pe"] = dev["q_nope"].clone(), dev["q_pe"].clone()
+        devs.append(d2)
+    B, H = inp.batch, inp.heads
+    outs = [torch.empty((B, H, 512), dtype=dev["q_nope"].dtype, device="cuda") for _ in devs]
+    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in devs]
+    desc = mla.make_desc(dev["q_nope"], dev["q_pe"], dev["kv_latent"], dev["k_pe"], dev["block_table"], outs[0])
+    ws = torch.empty(mla.mla_workspace_size(desc, args.num_split, mla.mla_num_cus()), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        d = devs[i % len(devs)]
+        mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], d["cache_seqlens"],
+                       inp.softmax_scale, num_split=args.num_split, out=outs[i % len(devs)],
+                       lse=lses[i % len(devs)], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations from HIP events recorded by the library on the launch stream.
+    mla.mla_timing_enable(True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    plan_ms, split_ms, comb_ms, calls = mla.mla_timing_read()
+    mla.mla_timing_enable(False)
+    split_avg = split_ms / max(calls, 1)
+
+    check = None
+    if args.check:
+        import oracle
+        from mla_inputs.torch_io import from_device
+        b = [0, B - 1]
+        ro, rl = oracle.mla_decode_ref(inp, batches=b)
+        o = from_device(outs[0][b])
+        l = from_device(lses[0][b])
+        ex = float((np.abs(o - ro) - (2e-3 + 1e-2 * np.abs(ro))).max())
+        check = {"sequences": b, "max_excess_out": ex, "max_lse_err": float(np.abs(l - rl).max()), "ok": ex <= 0}
+
+    cpu = cpu_baseline(inp, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    tflops = flops / (ms * 1e-3) / 1e12
+    ai = flops / total_bytes
+    roof_tflops = min(HBM_PEAK_GBS * 1e9 * ai / 1e12, MFMA_PEAK_TFLOPS)
+    split_gbs = total_bytes / (split_avg * 1e-3) / 1e9 if split_avg > 0 else None
+    mean_L = float(np.mean(inp.cache_seqlens))
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded N(0,1), no dataset)",
+        "config": {"workload": mi.CONFIG_NAMES[args.config], "batch": B, "heads": H,
+                   "seqlen_kv_mean": mean_L, "layout": "paged" if inp.paged else "contiguous",
+                   "num_split": args.num_split or "planner", "input_copies": len(devs)},
+        "us_per_call": round(ms * 1e3, 2),
+        "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+        "arith_intensity": round(ai, 1),
+        "roofline_tflops": round(roof_tflops, 1),
+        "frac_of_roofline": round(tflops / roof_tflops, 4),
+        "kernel_ms": {"plan": plan_ms / max(calls, 1), "split": split_avg, "combine": comb_ms / max(calls, 1)},
+        "roofline": {"bound": "hbm", "achieved": None if split_gbs is None else round(split_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": None if split_gbs is None else round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "split_kernel"},
+        "cpu_baseline": cpu,
+        "input_gen_s": round(gen_s, 1),
+    }
+    if check is not None:
+        line["check"] = check
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,220 @@
+"""MI355X (gfx950) DeepSeek MLA decode.
+
+Thin Python binding over the C ABI of ``libmla_decode.so``: it reads shapes and
+strides off PyTorch tensors, allocates outputs and workspace with PyTorch, and
+passes raw device pointers and the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    D_LATENT,
+    D_ROPE,
+    MAX_SPLITS,
+    MLA_DTYPE_BF16,
+    MLA_DTYPE_F16,
+    SPLIT_BLOCK_ROWS,
+    MlaDesc,
+    MlaError,
+)
+
+__all__ = [
+    "mla_decode", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
+    "mla_num_cus", "mla_last_error", "mla_timing_enable", "mla_timing_read", "make_desc",
+    "MlaDesc", "MlaError",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return MLA_DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float16 or bfloat16")
+
+
+def _as4(t, last: int, name: str):
+    """View a cache tensor as [N, rows, 1, last] (accepts [N, rows, last] too)."""
+    if t.dim() == 3:
+        t = t.unsqueeze(2)
+    if t.dim() != 4 or t.shape[2] != 1 or t.shape[3] != last:
+        raise ValueError(f"{name} must be [N, rows, 1, {last}] (one KV head), got {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} last dimension must be contiguous")
+    return t
+
+
+def mla_last_error() -> str:
+    return _lib.lib().mla_last_error().decode(errors="replace")
+
+
+def mla_num_cus(device: Optional[int] = None) -> int:
+    torch = _torch()
+    dev = torch.cuda.current_device() if device is None else int(device)
+    n = ctypes.c_int32()
+    _lib.check(_lib.lib().mla_num_cus(dev, ctypes.byref(n)))
+    return n.value
+
+
+def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out) -> MlaDesc:
+    """Fill an ``MlaDesc`` from tensors (strides in elements)."""
+    if q_nope.dim() != 3 or q_nope.shape[2] != D_LATENT or q_nope.stride(2) != 1:
+        raise ValueError(f"q_nope must be [B, H, 512] with contiguous last dim, got {tuple(q_nope.shape)}")
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    if tuple(q_pe.shape) != (B, H, D_ROPE) or q_pe.stride(2) != 1:
+        raise ValueError(f"q_pe must be [B, H, 64], got {tuple(q_pe.shape)}")
+    if tuple(out.shape) != (B, H, D_LATENT) or out.stride(2) != 1:
+        raise ValueError(f"out must be [B, H, 512], got {tuple(out.shape)}")
+    kv = _as4(kv_latent, D_LATENT, "kv_latent")
+    kp = _as4(k_pe, D_ROPE, "k_pe")
+    if kv.shape[:2] != kp.shape[:2]:
+        raise ValueError("kv_latent and k_pe disagree on [N, rows]")
+    d = MlaDesc()
+    d.batch, d.heads = B, H
+    d.d_latent, d.d_rope = D_LATENT, D_ROPE
+    d.dtype = _dtype_code(q_nope)
+    for t, nm in ((q_pe, "q_pe"), (kv, "kv_latent"), (kp, "k_pe"), (out, "out")):
+        if t.dtype != q_nope.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} differs from q_nope dtype {q_nope.dtype}")
+    if block_table is None:
+        if kv.shape[0] != B:
+            raise ValueError("contiguous cache must have batch as its first dimension")
+        d.max_seqlen = kv.shape[1]
+    else:
+        d.page_block_size = kv.shape[1]
+        d.block_table_stride = block_table.stride(0)
+        d.num_pages = kv.shape[0]
+    d.q_nope_sb, d.q_nope_sh = q_nope.stride(0), q_nope.stride(1)
+    d.q_pe_sb, d.q_pe_sh = q_pe.stride(0), q_pe.stride(1)
+    d.kv_sb, d.kv_sr = kv.stride(0), kv.stride(1)
+    d.kpe_sb, d.kpe_sr = kp.stride(0), kp.stride(1)
+    d.out_sb, d.out_sh = out.stride(0), out.stride(1)
+    return d
+
+
+def mla_max_work(desc: MlaDesc, num_split: int, num_cus: int) -> int:
+    n = ctypes.c_int32()
+    _lib.check(_lib.lib().mla_max_work(ctypes.byref(desc), int(num_split), int(num_cus), ctypes.byref(n)))
+    return n.value
+
+
+def mla_workspace_size(desc: MlaDesc, num_split: int, num_cus: int) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.lib().mla_workspace_size(ctypes.byref(desc), int(num_split), int(num_cus), ctypes.byref(n)))
+    return n.value
+
+
+_workspaces = {}
+
+
+def _workspace(device, stream_id: int, nbytes: int):
+    torch = _torch()
+    key = (device, stream_id)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
+               num_split: int = 0, out=None, lse=None, workspace=None,
+               stream=None) -> Tuple["object", "object"]:
+    """MLA decode through the C ABI; returns ``(out [B,H,512], lse fp32 [B,H])``.
+
+    Contiguous cache: ``kv_latent [B, S, 1, 512]``, ``k_pe [B, S, 1, 64]``,
+    ``block_table=None``.  Paged cache: ``kv_latent`` / ``k_pe`` are views of a
+    pool ``[P, page, 1, 576]`` (``pool[..., :512]`` and ``pool[..., 512:]``)
+    and ``block_table`` is int32 ``[B, max_blocks]``.  ``num_split=0`` lets the
+    planner choose the splits.  Work is enqueued on ``stream`` (default: the
+    current stream) and nothing synchronises.
+    """
+    torch = _torch()
+    if not q_nope.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    if out is None:
+        out = torch.empty((B, H, D_LATENT), dtype=q_nope.dtype, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H):
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous int32 tensor")
+    if block_table is not None and (block_table.dtype != torch.int32 or block_table.stride(1) != 1):
+        raise ValueError("block_table must be int32 with contiguous rows")
+    desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out)
+    s = torch.cuda.current_stream(q_nope.device) if stream is None else stream
+    if workspace is None:
+        need = mla_workspace_size(desc, num_split, mla_num_cus(q_nope.device.index))
+        workspace = _workspace(q_nope.device, s.cuda_stream, need)
+    kv = _as4(kv_latent, D_LATENT, "kv_latent")
+    kp = _as4(k_pe, D_ROPE, "k_pe")
+    st = _lib.lib().mla_decode(
+        q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(),
+        None if block_table is None else block_table.data_ptr(), cache_seqlens.data_ptr(),
+        float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), s.cuda_stream)
+    _lib.check(st)
+    return out, lse
+
+
+def mla_plan_host(cache_seqlens, heads: int, num_split: int, num_cus: int):
+    """Host twin of the planner.  Returns (num_splits [B], split_offset [B+1], work [W, 4]) as numpy."""
+    import numpy as np
+    lens = np.ascontiguousarray(cache_seqlens, dtype=np.int32)
+    B = lens.shape[0]
+    if num_split > 0:
+        max_work = B * num_split
+    else:
+        hg = -(-heads // 128)
+        max_work = max(B, -(-num_cus // hg))
+    ns = np.zeros(B, np.int32)
+    off = np.zeros(B + 1, np.int32)
+    work = np.zeros((max(max_work, 1), 4), np.int32)
+    _lib.check(_lib.lib().mla_plan_host(
+        lens.ctypes.data, B, int(heads), int(num_split), int(num_cus), ns.ctypes.data, off.ctypes.data,
+        work.ctypes.data, int(max_work)))
+    return ns, off, work[:off[B]]
+
+
+def mla_plan_device(cache_seqlens, heads: int, num_split: int, num_cus: int, stream=None):
+    """Device planner; returns (num_splits, split_offset, work) as torch tensors on the GPU."""
+    torch = _torch()
+    B = cache_seqlens.shape[0]
+    if num_split > 0:
+        max_work = B * num_split
+    else:
+        hg = -(-heads // 128)
+        max_work = max(B, -(-num_cus // hg))
+    dev = cache_seqlens.device
+    ns = torch.zeros(B, dtype=torch.int32, device=dev)
+    off = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+    work = torch.zeros((max(max_work, 1), 4), dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    _lib.check(_lib.lib().mla_plan_device(
+        cache_seqlens.data_ptr(), B, int(heads), int(num_split), int(num_cus), ns.data_ptr(), off.data_ptr(),
+        work.data_ptr(), int(max_work), s.cuda_stream))
+    return ns, off, work
+
+
+def mla_timing_enable(enable: bool = True) -> None:
+    _lib.check(_lib.lib().mla_timing_enable(1 if enable else 0))
+
+
+def mla_timing_read():
+    """(plan_ms, split_ms, combine_ms, calls) summed since the last read."""
+    a, b, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    n = ctypes.c_int32()
+    _lib.check(_lib.lib().mla_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(n)))
+    return a.value, b.value, c.value, n.value

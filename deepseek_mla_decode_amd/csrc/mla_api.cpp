@@ -1,0 +1,382 @@
+// mla_api.cpp -- host side of the MLA decode C ABI: argument validation,
+// workspace layout, the host twin of the split planner, launches and timing.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mla_decode.h"
+#include "mla_kernels.h"
+#include "plan_rule.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_num_cus[kMaxDevices];
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout: [plan ints][partial lse fp32][partial out fp32].
+struct Layout {
+  size_t num_splits, split_offset, work, part_lse, part_o, total;
+};
+
+Layout layout(const mla_desc* d, int32_t max_work) {
+  Layout L;
+  const size_t B = (size_t)d->batch, H = (size_t)d->heads, W = (size_t)max_work;
+  L.num_splits = 0;
+  L.split_offset = L.num_splits + B * 4;
+  L.work = L.split_offset + (B + 1) * 4;
+  L.part_lse = round_up(L.work + 4 * W * 4, 256);
+  L.part_o = round_up(L.part_lse + W * H * 4, 256);
+  L.total = round_up(L.part_o + W * H * 512 * 4, 256);
+  return L;
+}
+
+int check_desc(const mla_desc* d) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", d->batch);
+  if (d->heads < 1) return fail(MLA_ERR_INVALID_ARG, "heads %d < 1", d->heads);
+  if (d->d_latent != MLA_D_LATENT || d->d_rope != MLA_D_ROPE)
+    return fail(MLA_ERR_UNSUPPORTED, "dims %d/%d: only 512 latent + 64 rope are supported", d->d_latent,
+                d->d_rope);
+  if (d->dtype != MLA_DTYPE_F16 && d->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+  return MLA_OK;
+}
+
+int check_num_split(int32_t num_split) {
+  if (num_split < 0 || num_split > MLA_MAX_SPLITS)
+    return fail(MLA_ERR_INVALID_ARG, "num_split %d outside [0, %d]", num_split, MLA_MAX_SPLITS);
+  return MLA_OK;
+}
+
+int max_work_of(const mla_desc* d, int32_t num_split, int32_t num_cus, int32_t* out) {
+  if (num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "num_cus %d < 1", num_cus);
+  int64_t w = num_split > 0 ? (int64_t)d->batch * num_split : (int64_t)mla::planner_cap(d->batch, d->heads, num_cus);
+  if (w > (int64_t)INT32_MAX / 4) return fail(MLA_ERR_INVALID_ARG, "too many work items (%lld)", (long long)w);
+  *out = (int32_t)w;
+  return MLA_OK;
+}
+
+// ---- timing ----------------------------------------------------------------
+constexpr int kMaxTimed = 4096;
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_events;  // 4 per call
+int g_timed = 0;
+
+hipEvent_t* timing_slot() {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing || g_timed >= kMaxTimed) return nullptr;
+  const size_t need = 4 * (size_t)(g_timed + 1);
+  while (g_events.size() < need) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_events.push_back(e);
+  }
+  return &g_events[4 * (size_t)g_timed++];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+int mla_num_cus(int device, int32_t* num_cus_out) {
+  if (!num_cus_out) return fail(MLA_ERR_INVALID_ARG, "num_cus_out is NULL");
+  if (device < 0 || device >= kMaxDevices) return fail(MLA_ERR_INVALID_ARG, "device %d out of range", device);
+  int32_t v = g_num_cus[device].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess || n <= 0)
+      return fail(MLA_ERR_HIP, "hipDeviceGetAttribute(multiProcessorCount): %s", hipGetErrorString(e));
+    v = n;
+    g_num_cus[device].store(v, std::memory_order_relaxed);
+  }
+  *num_cus_out = v;
+  return ok();
+}
+
+int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32_t* max_work_out) {
+  int st;
+  if ((st = check_desc(desc)) != MLA_OK) return st;
+  if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (!max_work_out) return fail(MLA_ERR_INVALID_ARG, "max_work_out is NULL");
+  if ((st = max_work_of(desc, num_split, num_cus, max_work_out)) != MLA_OK) return st;
+  return ok();
+}
+
+int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out) {
+  int st;
+  if ((st = check_desc(desc)) != MLA_OK) return st;
+  if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (!bytes_out) return fail(MLA_ERR_INVALID_ARG, "bytes_out is NULL");
+  int32_t w;
+  if ((st = max_work_of(desc, num_split, num_cus, &w)) != MLA_OK) return st;
+  *bytes_out = layout(desc, w).total;
+  return ok();
+}
+
+int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
+                  int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+                  int32_t max_work) {
+  int st;
+  if (batch < 0 || heads < 1 || num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "bad batch/heads/num_cus");
+  if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (batch > 0 && (!cache_seqlens || !num_splits || !work)) return fail(MLA_ERR_INVALID_ARG, "NULL array");
+  if (!split_offset) return fail(MLA_ERR_INVALID_ARG, "NULL split_offset");
+  const int32_t cap_rows = INT32_MAX;
+  std::vector<int32_t> nb(batch);
+  int32_t mx = 0;
+  for (int b = 0; b < batch; ++b) {
+    nb[b] = mla::num_blocks(mla::clamp_len(cache_seqlens[b], cap_rows));
+    mx = nb[b] > mx ? nb[b] : mx;
+  }
+  int32_t t = 1;
+  if (num_split == 0) {
+    const int64_t cap = mla::planner_cap(batch, heads, num_cus);
+    int32_t lo = 1, hi = mx > 1 ? mx : 1;
+    while (lo < hi) {
+      const int32_t mid = lo + (hi - lo) / 2;
+      int64_t cnt = 0;
+      for (int b = 0; b < batch; ++b) cnt += mla::splits_for_budget(nb[b], mid);
+      if (cnt <= cap) hi = mid; else lo = mid + 1;
+    }
+    t = lo;
+  }
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) total += num_split > 0 ? num_split : mla::splits_for_budget(nb[b], t);
+  if (total > max_work) return fail(MLA_ERR_INVALID_ARG, "plan needs %lld work items > max_work %d",
+                                    (long long)total, max_work);
+  int32_t off = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t L = mla::clamp_len(cache_seqlens[b], cap_rows);
+    const int32_t s = num_split > 0 ? num_split : mla::splits_for_budget(nb[b], t);
+    num_splits[b] = s;
+    split_offset[b] = off;
+    for (int32_t k = 0; k < s; ++k) {
+      int32_t r0, r1;
+      mla::split_range(L, s, k, &r0, &r1);
+      int32_t* w = work + 4 * (size_t)(off + k);
+      w[0] = b;
+      w[1] = k;
+      w[2] = r0;
+      w[3] = r1;
+    }
+    off += s;
+  }
+  split_offset[batch] = off;
+  return ok();
+}
+
+int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
+                    int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+                    int32_t max_work, hipStream_t stream) {
+  int st;
+  if (batch < 0 || heads < 1 || num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "bad batch/heads/num_cus");
+  if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (batch > 0 && (!cache_seqlens || !num_splits || !work)) return fail(MLA_ERR_INVALID_ARG, "NULL array");
+  if (!split_offset) return fail(MLA_ERR_INVALID_ARG, "NULL split_offset");
+  const int64_t need = num_split > 0 ? (int64_t)batch * num_split : mla::planner_cap(batch, heads, num_cus);
+  if (need > max_work) return fail(MLA_ERR_INVALID_ARG, "max_work %d < %lld", max_work, (long long)need);
+  mla::PlanParams p{};
+  p.seqlens = cache_seqlens;
+  p.num_splits = num_splits;
+  p.split_offset = split_offset;
+  p.work = work;
+  p.batch = batch;
+  p.heads = heads;
+  p.num_split = num_split;
+  p.num_cus = num_cus;
+  p.row_cap = INT32_MAX;
+  hipError_t e = mla::launch_plan(p, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+               const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+               int32_t num_split, void* out, float* lse, const mla_desc* d, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_desc(d)) != MLA_OK) return st;
+  if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (d->batch == 0) return ok();
+  if (!q_nope || !q_pe || !kv_latent || !k_pe || !cache_seqlens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "NULL data pointer");
+  const int64_t strides[] = {d->q_nope_sb, d->q_nope_sh, d->q_pe_sb, d->q_pe_sh, d->kv_sb,
+                             d->kv_sr,     d->kpe_sb,    d->kpe_sr,  d->out_sb,  d->out_sh};
+  for (int64_t s : strides) {
+    if (s < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride %lld", (long long)s);
+    if (s % 8) return fail(MLA_ERR_UNSUPPORTED, "stride %lld is not a multiple of 8 elements", (long long)s);
+  }
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(kv_latent, 16) || !aligned(k_pe, 16) ||
+      !aligned(out, 16))
+    return fail(MLA_ERR_UNSUPPORTED, "q/cache/out pointers must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cache_seqlens, 4) || (block_table && !aligned(block_table, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "lse/cache_seqlens/block_table must be 4-byte aligned");
+  const bool paged = block_table != nullptr;
+  int32_t row_cap;
+  if (paged) {
+    if (d->page_block_size < 32 || d->page_block_size % 32)
+      return fail(MLA_ERR_UNSUPPORTED, "page_block_size %d must be a positive multiple of 32", d->page_block_size);
+    if (d->block_table_stride < 1) return fail(MLA_ERR_INVALID_ARG, "block_table_stride < 1");
+    if (d->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages < 1");
+    const int64_t cap = (int64_t)d->block_table_stride * d->page_block_size;
+    row_cap = cap > INT32_MAX ? INT32_MAX : (int32_t)cap;
+  } else {
+    if (d->max_seqlen < 0) return fail(MLA_ERR_INVALID_ARG, "max_seqlen < 0");
+    row_cap = d->max_seqlen;
+  }
+
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int32_t num_cus = 0;
+  if ((st = mla_num_cus(device, &num_cus)) != MLA_OK) return st;
+  int32_t max_work;
+  if ((st = max_work_of(d, num_split, num_cus, &max_work)) != MLA_OK) return st;
+  const Layout L = layout(d, max_work);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? workspace_bytes : 0, L.total);
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* num_splits = reinterpret_cast<int32_t*>(ws + L.num_splits);
+  int32_t* split_offset = reinterpret_cast<int32_t*>(ws + L.split_offset);
+  int32_t* work = reinterpret_cast<int32_t*>(ws + L.work);
+  float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  float* part_o = reinterpret_cast<float*>(ws + L.part_o);
+
+  hipEvent_t* ev = timing_slot();
+  if (ev) (void)hipEventRecord(ev[0], stream);
+
+  if (num_split == 0) {
+    mla::PlanParams pp{};
+    pp.seqlens = cache_seqlens;
+    pp.num_splits = num_splits;
+    pp.split_offset = split_offset;
+    pp.work = work;
+    pp.batch = d->batch;
+    pp.heads = d->heads;
+    pp.num_split = 0;
+    pp.num_cus = num_cus;
+    pp.row_cap = row_cap;
+    if ((e = mla::launch_plan(pp, stream)) != hipSuccess)
+      return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  }
+  if (ev) (void)hipEventRecord(ev[1], stream);
+
+  mla::SplitParams sp{};
+  sp.q_nope = static_cast<const uint16_t*>(q_nope);
+  sp.q_pe = static_cast<const uint16_t*>(q_pe);
+  sp.kv = static_cast<const uint16_t*>(kv_latent);
+  sp.kpe = static_cast<const uint16_t*>(k_pe);
+  sp.block_table = block_table;
+  sp.seqlens = cache_seqlens;
+  sp.work = work;
+  sp.split_offset = split_offset;
+  sp.out = static_cast<uint16_t*>(out);
+  sp.lse = lse;
+  sp.part_o = part_o;
+  sp.part_lse = part_lse;
+  sp.q_nope_sb = d->q_nope_sb;
+  sp.q_nope_sh = d->q_nope_sh;
+  sp.q_pe_sb = d->q_pe_sb;
+  sp.q_pe_sh = d->q_pe_sh;
+  sp.kv_sb = d->kv_sb;
+  sp.kv_sr = d->kv_sr;
+  sp.kpe_sb = d->kpe_sb;
+  sp.kpe_sr = d->kpe_sr;
+  sp.out_sb = d->out_sb;
+  sp.out_sh = d->out_sh;
+  sp.num_split = num_split;
+  sp.batch = d->batch;
+  sp.heads = d->heads;
+  sp.page_size = paged ? d->page_block_size : 1;
+  sp.bt_stride = paged ? d->block_table_stride : 0;
+  sp.num_pages = paged ? d->num_pages : 0;
+  sp.row_cap = row_cap;
+  sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), stream)) != hipSuccess)
+    return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
+  if (ev) (void)hipEventRecord(ev[2], stream);
+
+  if (num_split != 1) {
+    mla::CombineParams cp{};
+    cp.part_o = part_o;
+    cp.part_lse = part_lse;
+    cp.split_offset = split_offset;
+    cp.out = static_cast<uint16_t*>(out);
+    cp.lse = lse;
+    cp.out_sb = d->out_sb;
+    cp.out_sh = d->out_sh;
+    cp.num_split = num_split;
+    cp.heads = d->heads;
+    if ((e = mla::launch_combine(cp, d->dtype, d->batch, stream)) != hipSuccess)
+      return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  }
+  if (ev) (void)hipEventRecord(ev[3], stream);
+  return ok();
+}
+
+int mla_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  g_timed = 0;
+  return ok();
+}
+
+int mla_timing_read(float* plan_ms, float* split_ms, float* combine_ms, int32_t* calls) {
+  if (!plan_ms || !split_ms || !combine_ms || !calls) return fail(MLA_ERR_INVALID_ARG, "NULL output");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double acc[3] = {0, 0, 0};
+  for (int i = 0; i < g_timed; ++i) {
+    hipEvent_t* ev = &g_events[4 * (size_t)i];
+    hipError_t e = hipEventSynchronize(ev[3]);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    for (int k = 0; k < 3; ++k) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[k], ev[k + 1]);
+      if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+      acc[k] += ms;
+    }
+  }
+  *plan_ms = (float)acc[0];
+  *split_ms = (float)acc[1];
+  *combine_ms = (float)acc[2];
+  *calls = g_timed;
+  g_timed = 0;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// mla_kernels.h -- kernel parameter blocks and launchers (library-internal).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/mla_decode.h"
+
+namespace mla {
+
+struct SplitParams {
+  const uint16_t* q_nope;
+  const uint16_t* q_pe;
+  const uint16_t* kv;           // latent part of cache rows
+  const uint16_t* kpe;          // RoPE part of cache rows
+  const int32_t* block_table;   // paged only
+  const int32_t* seqlens;
+  const int32_t* work;          // planner mode: work list (4 ints per item)
+  const int32_t* split_offset;  // planner mode: [B + 1]
+  uint16_t* out;
+  float* lse;
+  float* part_o;                // [max_work, H, 512]
+  float* part_lse;              // [max_work, H], base 2
+  int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
+  int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
+  int64_t out_sb, out_sh;
+  int32_t num_split;            // > 0 forced, 0 planner mode
+  int32_t batch, heads;
+  int32_t page_size, bt_stride;
+  int32_t num_pages;            // paged: page indices are clamped to [0, num_pages)
+  int32_t row_cap;              // lengths are clamped to [0, row_cap]
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* split_offset;  // planner mode
+  uint16_t* out;
+  float* lse;
+  int64_t out_sb, out_sh;
+  int32_t num_split;
+  int32_t heads;
+};
+
+struct PlanParams {
+  const int32_t* seqlens;
+  int32_t* num_splits;
+  int32_t* split_offset;
+  int32_t* work;
+  int32_t batch, heads, num_split, num_cus;
+  int32_t row_cap;              // lengths are clamped to [0, row_cap]
+};
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int dtype, int batch, hipStream_t stream);
+
+}  // namespace mla

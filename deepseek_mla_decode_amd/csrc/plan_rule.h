@@ -1,0 +1,56 @@
+// plan_rule.h -- integer rules of the split planner, shared by the host twin
+// (mla_api.cpp) and the device planner kernel (mla_kernels.hip) so that both
+// produce the same plan.
+//
+// Range rule: the TileLang MLA guide's paged variant cuts each sequence by
+// blocks_per_split / remaining_blocks ("Split-KV" item of its optimisation
+// list).  Here a sequence of L rows has nb = ceil(L / 64) blocks; split k of s
+// takes floor(nb / s) blocks, plus one more when k < nb mod s, in order.
+#pragma once
+
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define MLA_HD __host__ __device__ __forceinline__
+#else
+#define MLA_HD inline
+#endif
+
+namespace mla {
+
+constexpr int kSplitBlockRows = 64;
+constexpr int kMaxSplits = 1024;
+constexpr int kHeadsPerGroup = 128;
+
+MLA_HD int32_t ceil_div(int32_t a, int32_t b) { return (int32_t)(((int64_t)a + b - 1) / b); }
+
+MLA_HD int32_t clamp_len(int32_t L, int32_t cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+MLA_HD int32_t num_blocks(int32_t L) { return L <= 0 ? 0 : ceil_div(L, kSplitBlockRows); }
+
+// Rows [*r0, *r1) of split k out of s for a sequence of L rows.
+MLA_HD void split_range(int32_t L, int32_t s, int32_t k, int32_t* r0, int32_t* r1) {
+  const int32_t nb = num_blocks(L);
+  const int32_t per = nb / s, rem = nb % s;
+  const int32_t first = k * per + (k < rem ? k : rem);
+  const int32_t n = per + (k < rem ? 1 : 0);
+  const int64_t a = (int64_t)first * kSplitBlockRows, b = (int64_t)(first + n) * kSplitBlockRows;
+  *r0 = (int32_t)(a < L ? a : L);
+  *r1 = (int32_t)(b < L ? b : L);
+}
+
+// Splits given to a sequence of nb blocks when each work item may take up to t blocks.
+MLA_HD int32_t splits_for_budget(int32_t nb, int32_t t) {
+  int32_t s = nb <= 0 ? 1 : ceil_div(nb, t);
+  return s > kMaxSplits ? kMaxSplits : s;
+}
+
+MLA_HD int32_t head_groups(int32_t heads) { return ceil_div(heads, kHeadsPerGroup); }
+
+// Most work items the planner may emit (planner mode).
+MLA_HD int32_t planner_cap(int32_t batch, int32_t heads, int32_t num_cus) {
+  const int32_t per_group = ceil_div(num_cus, head_groups(heads));
+  return batch > per_group ? batch : per_group;
+}
+
+}  // namespace mla

@@ -1,0 +1,199 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) DeepSeek MLA decode library.
+ *
+ * The operation (one query token per sequence, one latent KV head shared by
+ * all query heads):
+ *
+ *   z[b,h,j]  = softmax_scale * ( q_nope[b,h,:] . latent_j + q_pe[b,h,:] . rope_j )
+ *   lse[b,h]  = ln sum_{j < L_b} exp(z[b,h,j])
+ *   out[b,h,:] = sum_{j < L_b} exp(z[b,h,j] - lse[b,h]) * latent_j
+ *
+ * where row j of sequence b's cache holds latent_j (512 values) and rope_j
+ * (64 values), L_b = cache_seqlens[b], and the value row is the latent part of
+ * the same cache row.  Sources: the TileLang MLA guide ("用 TileLang 编写高性能
+ * DeepSeek MLA 内核"), sections "先看核心难点" (Q/K width 576 = 512 + 64,
+ * V width 512), "Split Kernel" (two products summed into one score tile, base-2
+ * online softmax with softmax_scale*log2(e) folded in), "Combine Kernel"
+ * (log-sum-exp merge of split partials), "变体内核" (paged cache through
+ * block_table with positions at or past cache_seqlens masked); and the FlashMLA
+ * analysis ("DeepSeek开源周第一天：FlashMLA 深度分析"), whose parameter struct
+ * lists the fields carried by mla_desc below (strides, block_table,
+ * page_block_size, split metadata, partial-output buffers).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are plain HIP device addresses; host pointers are marked.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - Work is enqueued on `stream` only; no call synchronises the device.
+ *     Inputs must stay alive until the stream reaches the call.
+ *   - Return value: MLA_OK (0) or a negative mla_status.  On an argument error
+ *     nothing is enqueued.  mla_last_error() gives a thread-local message.
+ *   - Nothing is thrown across the ABI.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad stride, ...   */
+  MLA_ERR_UNSUPPORTED = -2,   /* dims other than 512/64, dtype, misalignment     */
+  MLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required      */
+  MLA_ERR_HIP = -4            /* a HIP runtime call or launch failed             */
+} mla_status;
+
+typedef enum mla_dtype {
+  MLA_DTYPE_F16 = 0,          /* IEEE binary16 for q, cache and out              */
+  MLA_DTYPE_BF16 = 1          /* bfloat16 for q, cache and out                   */
+} mla_dtype;
+
+/* Latent (value) width and RoPE width; the only supported sizes. */
+#define MLA_D_LATENT 512
+#define MLA_D_ROPE 64
+/* Split planning works in blocks of this many cache rows. */
+#define MLA_SPLIT_BLOCK_ROWS 64
+/* Largest number of splits of one sequence. */
+#define MLA_MAX_SPLITS 1024
+
+/*
+ * Problem description.  All strides are in ELEMENTS of the input dtype and must
+ * keep every row start 16-byte aligned (multiples of 8 elements).
+ *
+ * Contiguous cache (block_table == NULL):
+ *   kv_latent[b, j, 0, :] at kv_latent + b*kv_sb + j*kv_sr      (512 values)
+ *   k_pe     [b, j, 0, :] at k_pe      + b*kpe_sb + j*kpe_sr    (64 values)
+ *   for j < max_seqlen; every cache_seqlens[b] must be <= max_seqlen.
+ * Paged cache (block_table != NULL), FlashMLA-style pool [P, page, 1, 576]:
+ *   logical row j of sequence b is row (j % page_block_size) of physical page
+ *   p = block_table[b*block_table_stride + j/page_block_size]; its latent part
+ *   is at kv_latent + p*kv_sb + (j % page)*kv_sr and its RoPE part at
+ *   k_pe + p*kpe_sb + (j % page)*kpe_sr.  For a single pool pass
+ *   kv_latent = pool, k_pe = pool + 512, kv_sb = kpe_sb = page*576,
+ *   kv_sr = kpe_sr = 576.  page_block_size must be a positive multiple of 32.
+ *   Only entries for j < cache_seqlens[b] are read; other entries may hold
+ *   anything (e.g. -1).  Entries that are read must lie in [0, num_pages).
+ */
+typedef struct mla_desc {
+  int32_t batch;               /* B >= 0                                         */
+  int32_t heads;               /* H >= 1 query heads (one shared KV head)        */
+  int32_t d_latent;            /* must be 512                                    */
+  int32_t d_rope;              /* must be 64                                     */
+  int32_t dtype;               /* mla_dtype of q_nope, q_pe, cache and out       */
+  int32_t max_seqlen;          /* contiguous: rows per sequence in the cache     */
+  int32_t page_block_size;     /* paged: rows per page                           */
+  int32_t block_table_stride;  /* paged: int32 entries per block_table row       */
+  int32_t num_pages;           /* paged: pages in the pool (documents the bound) */
+  int32_t reserved;            /* must be 0                                      */
+  int64_t q_nope_sb, q_nope_sh;  /* q_nope[b,h,:]  at q_nope + b*sb + h*sh       */
+  int64_t q_pe_sb, q_pe_sh;      /* q_pe[b,h,:]    at q_pe + b*sb + h*sh         */
+  int64_t kv_sb, kv_sr;          /* latent: batch (or page) stride, row stride   */
+  int64_t kpe_sb, kpe_sr;        /* rope:   batch (or page) stride, row stride   */
+  int64_t out_sb, out_sh;        /* out[b,h,:]     at out + b*sb + h*sh          */
+} mla_desc;
+
+/*
+ * Split plan (what the planner writes; all int32, device- or host-resident).
+ * A "work item" is one KV range of one sequence for all heads:
+ *   work[4*w + 0] = b, work[4*w + 1] = split index k within b,
+ *   work[4*w + 2] = first cache row, work[4*w + 3] = one past the last row.
+ *   num_splits[b] = s_b; split_offset[b] = index of b's first work item, and
+ *   split_offset[B] = total work items W.
+ * Ranges follow the TileLang guide's paged variant ("Split-KV" item of its
+ * optimisation list: per-sequence blocks_per_split and remaining_blocks): the
+ * nb = ceil(L_b / 64) blocks of sequence b are dealt out in order, split k
+ * getting floor(nb / s_b) blocks plus one more when k < nb mod s_b.
+ *
+ * How s_b is chosen (num_split == 0, "planner" mode) is this library's own
+ * rule, meant to fill the compute units: one work item per CU is the target,
+ * so the planner finds the smallest per-item block budget t with
+ *   sum_b max(1, ceil(nb_b / t)) <= max(B, ceil(num_cus / head_groups))
+ * and sets s_b = max(1, ceil(nb_b / t)), capped at MLA_MAX_SPLITS.
+ * head_groups = ceil(H / 128).  With num_split > 0 every s_b = num_split,
+ * including splits that end up empty.
+ */
+
+/* Number of compute units of `device` (queried once, cached). */
+int mla_num_cus(int device, int32_t* num_cus_out /* host */);
+
+/*
+ * Upper bound on the work items a plan can have for this description:
+ *   num_split > 0 : B * num_split
+ *   num_split == 0: max(B, ceil(num_cus / head_groups))
+ */
+int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32_t* max_work_out /* host */);
+
+/*
+ * Bytes of device workspace mla_decode needs for this description:
+ *   plan (int32): B + (B+1) + 4*max_work, rounded to 256 bytes,
+ *   partial lse  (fp32, base 2):  max_work * H,
+ *   partial out  (fp32):          max_work * H * 512.
+ */
+int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
+
+/*
+ * Host twin of the planner: same integers as the device planner.
+ *   cache_seqlens  host int32[batch]
+ *   num_splits     host int32[batch]            (out)
+ *   split_offset   host int32[batch + 1]        (out)
+ *   work           host int32[4 * max_work]     (out)
+ *   max_work       capacity of `work` in items; MLA_ERR_INVALID_ARG if too small.
+ */
+int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
+                  int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+                  int32_t max_work);
+
+/*
+ * Device planner: one workgroup reads cache_seqlens (device int32[batch]) and
+ * writes num_splits / split_offset / work (device arrays as in mla_plan_host).
+ */
+int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
+                    int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+                    int32_t max_work, hipStream_t stream);
+
+/*
+ * MLA decode.  All array arguments are device pointers.
+ *   q_nope [B, H, 512], q_pe [B, H, 64]     dtype, strides in desc
+ *   kv_latent, k_pe                         cache (see mla_desc)
+ *   block_table  int32, NULL for a contiguous cache
+ *   cache_seqlens int32[B], each >= 0 (a negative length gives undefined output)
+ *   softmax_scale  multiplies the raw dot products (typically 1/sqrt(576))
+ *   num_split  0 = planner chooses s_b per sequence; > 0 forces s_b = num_split
+ *   out   [B, H, 512] dtype (strides in desc)
+ *   lse   fp32 [B, H] contiguous, natural log of the sum of exp(z)
+ *   workspace  device buffer of at least mla_workspace_size() bytes, 256-byte
+ *              aligned; its contents on entry do not matter.
+ * A sequence with L_b = 0 gets out = 0 and lse = -inf.
+ * Launches: planner (planner mode only), split kernel, combine kernel (only
+ * touches sequences with s_b > 1; a single split writes out/lse directly).
+ * Calls that share a workspace must be ordered on one stream.
+ */
+int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+               const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+               int32_t num_split, void* out, float* lse, const mla_desc* desc, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char* mla_last_error(void);
+
+/*
+ * Kernel timing for measurement.  While enabled, every mla_decode call records
+ * HIP events around its planner, split and combine launches on its stream.
+ * mla_timing_read() synchronises on those events and returns the summed
+ * milliseconds and the number of calls since the last read (then resets).
+ * Up to 4096 calls are recorded between reads; later ones are not timed.
+ */
+int mla_timing_enable(int enable);
+int mla_timing_read(float* plan_ms, float* split_ms, float* combine_ms, int32_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,200 @@
+"""C ABI checks that need no GPU: symbols, argument validation, workspace sizes,
+and the host twin of the split planner against the oracle's split ranges."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from deepseek_mla_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*|size_t)\s+\**(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in mla_decode.h but not exported"
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def _desc(B=2, H=16, dtype=0, **kw):
+    d = _lib.MlaDesc()
+    d.batch, d.heads, d.d_latent, d.d_rope, d.dtype = B, H, 512, 64, dtype
+    d.max_seqlen = 256
+    d.q_nope_sb, d.q_nope_sh = H * 512, 512
+    d.q_pe_sb, d.q_pe_sh = H * 64, 64
+    d.kv_sb, d.kv_sr = 256 * 512, 512
+    d.kpe_sb, d.kpe_sr = 256 * 64, 64
+    d.out_sb, d.out_sh = H * 512, 512
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _decode(L, desc, num_split=0, scale=1 / 24, ptrs=None, block_table=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(q=FAKE, qp=FAKE, kv=FAKE, kpe=FAKE, lens=FAKE, out=FAKE, lse=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return L.mla_decode(p["q"], p["qp"], p["kv"], p["kpe"], block_table, p["lens"], scale, num_split, p["out"],
+                        p["lse"], None if desc is None else ctypes.byref(desc), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", _lib.MLA_ERR_INVALID_ARG),
+    ("neg_batch", _lib.MLA_ERR_INVALID_ARG),
+    ("zero_heads", _lib.MLA_ERR_INVALID_ARG),
+    ("dims", _lib.MLA_ERR_UNSUPPORTED),
+    ("dtype", _lib.MLA_ERR_UNSUPPORTED),
+    ("reserved", _lib.MLA_ERR_INVALID_ARG),
+    ("neg_split", _lib.MLA_ERR_INVALID_ARG),
+    ("huge_split", _lib.MLA_ERR_INVALID_ARG),
+    ("nan_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("null_q", _lib.MLA_ERR_INVALID_ARG),
+    ("null_lens", _lib.MLA_ERR_INVALID_ARG),
+    ("stride_not_8", _lib.MLA_ERR_UNSUPPORTED),
+    ("neg_stride", _lib.MLA_ERR_INVALID_ARG),
+    ("misaligned_kv", _lib.MLA_ERR_UNSUPPORTED),
+    ("misaligned_lse", _lib.MLA_ERR_INVALID_ARG),
+    ("page_16", _lib.MLA_ERR_UNSUPPORTED),
+    ("page_stride0", _lib.MLA_ERR_INVALID_ARG),
+    ("neg_max_seqlen", _lib.MLA_ERR_INVALID_ARG),
+])
+def test_validation_errors(L, case, expect):
+    d = _desc()
+    kw = {}
+    if case == "null_desc":
+        d = None
+    elif case == "neg_batch":
+        d.batch = -1
+    elif case == "zero_heads":
+        d.heads = 0
+    elif case == "dims":
+        d.d_latent = 448
+    elif case == "dtype":
+        d.dtype = 7
+    elif case == "reserved":
+        d.reserved = 1
+    elif case == "neg_split":
+        kw["num_split"] = -1
+    elif case == "huge_split":
+        kw["num_split"] = _lib.MAX_SPLITS + 1
+    elif case == "nan_scale":
+        kw["scale"] = float("nan")
+    elif case == "null_q":
+        kw["ptrs"] = {"q": None}
+    elif case == "null_lens":
+        kw["ptrs"] = {"lens": None}
+    elif case == "stride_not_8":
+        d.kv_sr = 516
+    elif case == "neg_stride":
+        d.out_sh = -512
+    elif case == "misaligned_kv":
+        kw["ptrs"] = {"kv": FAKE + 2}
+    elif case == "misaligned_lse":
+        kw["ptrs"] = {"lse": FAKE + 2}
+    elif case == "page_16":
+        d.page_block_size, d.block_table_stride, d.num_pages = 16, 4, 8
+        kw["block_table"] = FAKE
+    elif case == "page_stride0":
+        d.page_block_size, d.block_table_stride, d.num_pages = 64, 0, 8
+        kw["block_table"] = FAKE
+    elif case == "neg_max_seqlen":
+        d.max_seqlen = -1
+    st = _decode(L, d, **kw)
+    assert st == expect, (case, st, L.mla_last_error())
+    assert L.mla_last_error().decode()
+
+
+def test_empty_batch_is_ok_without_touching_memory(L):
+    d = _desc(B=0)
+    assert _decode(L, d, ptrs={k: None for k in ("q", "qp", "kv", "kpe", "lens", "out", "lse")}) == _lib.MLA_OK
+
+
+def test_workspace_size_formula(L):
+    for B, H, ns, cus in [(2, 16, 1, 256), (64, 128, 0, 256), (2, 128, 64, 256), (3, 200, 0, 256), (500, 128, 0, 256)]:
+        d = _desc(B=B, H=H)
+        w = ctypes.c_int32()
+        assert L.mla_max_work(ctypes.byref(d), ns, cus, ctypes.byref(w)) == 0
+        hg = -(-H // 128)
+        want_w = B * ns if ns else max(B, -(-cus // hg))
+        assert w.value == want_w
+        n = ctypes.c_size_t()
+        assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0
+        r = lambda x: -(-x // 256) * 256  # noqa: E731
+        plan = 4 * B + 4 * (B + 1) + 16 * want_w
+        part_lse = r(plan)
+        part_o = r(part_lse + 4 * want_w * H)
+        assert n.value == r(part_o + 2048 * want_w * H)
+
+
+def _plan(lens, heads, ns, cus):
+    from deepseek_mla_decode_amd import mla_plan_host
+    return mla_plan_host(np.asarray(lens, np.int32), heads, ns, cus)
+
+
+def _check_ranges_against_oracle(lens, ns_arr, off, work):
+    for b, L_b in enumerate(lens):
+        s = int(ns_arr[b])
+        want = oracle.split_ranges(int(max(L_b, 0)), s)
+        got = [(int(work[off[b] + k, 2]), int(work[off[b] + k, 3])) for k in range(s)]
+        assert got == want, (b, L_b, s)
+        assert all(int(work[off[b] + k, 0]) == b and int(work[off[b] + k, 1]) == k for k in range(s))
+
+
+@pytest.mark.parametrize("lens,heads,ns", [
+    ([256, 256], 16, 1), ([256, 256], 16, 4), ([4096] * 64, 128, 0), ([8192] * 128, 128, 0),
+    ([131072] * 2, 128, 0), ([131072] * 2, 128, 64), ([1, 0, 65, 64, 63, 300], 128, 0),
+    ([0, 0, 0], 128, 0), ([5, 7], 128, 8),
+])
+def test_host_planner_matches_oracle_ranges(lens, heads, ns):
+    nsa, off, work = _plan(lens, heads, ns, 256)
+    assert off[0] == 0 and int(off[-1]) == work.shape[0]
+    if ns:
+        assert (nsa == ns).all()
+    _check_ranges_against_oracle(lens, nsa, off, work)
+
+
+def test_planner_fills_the_cus_for_uniform_lengths():
+    for lens, want in (([4096] * 64, 4), ([8192] * 128, 2), ([131072] * 2, 128)):
+        nsa, off, _ = _plan(lens, 128, 0, 256)
+        assert (nsa == want).all() and int(off[-1]) == 256
+
+
+def test_planner_budget_is_minimal_on_random_lengths():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(0, 20000, size=B).astype(np.int32)
+        heads = int(rng.choice([16, 64, 128, 256]))
+        cus = int(rng.choice([80, 256, 304]))
+        nsa, off, work = _plan(lens, heads, 0, cus)
+        hg = -(-heads // 128)
+        cap = max(B, -(-cus // hg))
+        assert int(off[-1]) <= cap and (nsa >= 1).all()
+        nb = -(-lens.astype(np.int64) // 64)
+        # the largest work item is at most t blocks, and with t - 1 the split total would exceed cap
+        t = max(int(max(-(-n // s) for n, s in zip(nb, nsa))), 1)
+        if t > 1:
+            assert sum(max(1, -(-int(n) // (t - 1))) for n in nb) > cap
+        _check_ranges_against_oracle(lens, nsa, off, work)

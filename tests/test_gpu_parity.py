@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (elementwise): |out - ref| <= 2e-3 + 1e-2 |ref| and |lse - ref| <= 1e-3;
+page indexing and split/combine bookkeeping are checked exactly (bitwise
+identity under page permutation, device plan == host plan).
+"""
+import numpy as np
+import pytest
+
+import mla_inputs as mi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_TOL = 2e-3, 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import deepseek_mla_decode_amd as m
+    m._lib.lib()   # loud failure if the library is missing
+    return m
+
+
+def _run(mla, inp, num_split, dev=None):
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    d = dev or to_device(inp, "cuda")
+    out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"],
+                              d["cache_seqlens"], inp.softmax_scale, num_split=num_split)
+    torch.cuda.synchronize()
+    return from_device(out), from_device(lse)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, what=""):
+    assert out.shape == ref_out.shape and lse.shape == ref_lse.shape
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    excess = np.abs(out - ref_out) - (ATOL + RTOL * np.abs(ref_out))
+    assert excess.max() <= 0, f"{what}: out off by {excess.max():.3e} beyond tolerance at {np.unravel_index(excess.argmax(), excess.shape)}"
+    both_inf = np.isneginf(lse) & np.isneginf(ref_lse)
+    err = np.where(both_inf, 0.0, np.abs(lse - ref_lse))
+    assert not np.isnan(err).any() and err.max() <= LSE_TOL, f"{what}: lse err {np.nanmax(err):.3e}"
+
+
+# ---------------------------------------------------------------------------
+# Small cases (the oracle computes every output)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_split", [1, 4, 0])
+def test_tiny_config(mla, num_split):
+    inp = mi.make_config(0)
+    out, lse = _run(mla, inp, num_split)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"tiny split={num_split}")
+
+
+def test_tiny_split_counts_agree(mla):
+    inp = mi.make_config(0)
+    o1, l1 = _run(mla, inp, 1)
+    o4, l4 = _run(mla, inp, 4)
+    assert_parity(o4, l4, o1, l1, "split 4 vs split 1")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("num_split", [0, 1, 3, 8])
+def test_ragged_lengths(mla, dtype, num_split):
+    lens = [0, 1, 31, 32, 33, 100, 64, 65, 200, 257]
+    inp = mi.make_contiguous(len(lens), 128, 260, lens, dtype, seed=101)
+    out, lse = _run(mla, inp, num_split)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"ragged {dtype} split={num_split}")
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+
+
+@pytest.mark.parametrize("heads", [1, 16, 33, 96, 128, 160, 256])
+def test_head_counts(mla, heads):
+    inp = mi.make_contiguous(3, heads, 150, [150, 77, 5], "f16", seed=102)
+    for ns in (0, 2):
+        out, lse = _run(mla, inp, ns)
+        ro, rl = oracle.mla_decode_ref(inp)
+        assert_parity(out, lse, ro, rl, f"heads={heads} split={ns}")
+
+
+@pytest.mark.parametrize("page", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_paged(mla, page, dtype):
+    lens = [1, 64, 129, 500, 1000, 33]
+    inp = mi.make_paged(len(lens), 128, lens, dtype, seed=103, page_block_size=page, spare_pages=5)
+    for ns in (0, 1, 5):
+        out, lse = _run(mla, inp, ns)
+        ro, rl = oracle.mla_decode_ref(inp)
+        assert_parity(out, lse, ro, rl, f"paged page={page} {dtype} split={ns}")
+
+
+def test_page_permutation_is_bitwise_invariant(mla):
+    lens = [700, 64, 1, 333]
+    inp = mi.make_paged(len(lens), 128, lens, "bf16", seed=104, page_block_size=64, spare_pages=3)
+    o0, l0 = _run(mla, inp, 0)
+    P = inp.pool.shape[0]
+    perm = np.random.default_rng(7).permutation(P)
+    pool2 = np.empty_like(inp.pool)
+    pool2[perm] = inp.pool
+    inp.block_table = np.where(inp.block_table >= 0, perm[np.maximum(inp.block_table, 0)], -1).astype(np.int32)
+    inp.pool = pool2
+    o1, l1 = _run(mla, inp, 0)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_seqlen_one_returns_the_value_row(mla):
+    for dtype in ("f16", "bf16"):
+        inp = mi.make_contiguous(4, 128, 32, [1, 1, 1, 1], dtype, seed=105)
+        out, lse = _run(mla, inp, 0)
+        v0 = oracle.to_f64(inp.kv_latent[:, 0, 0, :], dtype)
+        assert np.array_equal(out, np.broadcast_to(v0[:, None, :], out.shape))
+        _, rl = oracle.mla_decode_ref(inp)
+        assert np.abs(lse - rl).max() <= LSE_TOL
+
+
+def test_more_splits_than_blocks(mla):
+    inp = mi.make_contiguous(3, 128, 100, [100, 1, 0], "bf16", seed=106)
+    out, lse = _run(mla, inp, 16)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, "16 splits of <= 2 blocks")
+
+
+def test_run_to_run_bitwise_deterministic(mla):
+    from mla_inputs.torch_io import to_device
+    inp = mi.make_paged(5, 128, [3000, 10, 900, 4096, 1], "bf16", seed=107, page_block_size=64)
+    dev = to_device(inp, "cuda")
+    o0, l0 = _run(mla, inp, 0, dev)
+    for _ in range(3):
+        o1, l1 = _run(mla, inp, 0, dev)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_strided_tensors(mla):
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    inp = mi.make_contiguous(3, 64, 96, [96, 50, 7], "f16", seed=108)
+    d = to_device(inp, "cuda")
+    # Queries as slices of a wider buffer, output into a strided view.
+    qbig = torch.zeros((3, 64, 1024), dtype=torch.float16, device="cuda")
+    qbig[:, :, 256:768] = d["q_nope"]
+    qpe_big = torch.zeros((3, 64, 128), dtype=torch.float16, device="cuda")
+    qpe_big[:, :, 64:] = d["q_pe"]
+    obig = torch.full((3, 64, 640), 7.0, dtype=torch.float16, device="cuda")
+    out = obig[:, :, 64:576]
+    lse = torch.empty((3, 64), dtype=torch.float32, device="cuda")
+    mla.mla_decode(qbig[:, :, 256:768], qpe_big[:, :, 64:], d["kv_latent"], d["k_pe"], None,
+                   d["cache_seqlens"], inp.softmax_scale, num_split=2, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(from_device(out), from_device(lse), ro, rl, "strided")
+    assert (obig[:, :, :64] == 7).all() and (obig[:, :, 576:] == 7).all()
+
+
+def test_device_planner_matches_host_twin(mla):
+    import torch
+    rng = np.random.default_rng(9)
+    for B, heads, ns, cus in [(64, 128, 0, 256), (3, 16, 0, 256), (200, 128, 0, 304), (7, 256, 0, 256),
+                              (5, 128, 6, 256), (1500, 128, 0, 256), (2, 128, 0, 256)]:
+        lens = rng.integers(0, 40000, size=B).astype(np.int32)
+        hn, ho, hw = mla.mla_plan_host(lens, heads, ns, cus)
+        dn, do, dw = mla.mla_plan_device(torch.from_numpy(lens).cuda(), heads, ns, cus)
+        torch.cuda.synchronize()
+        assert np.array_equal(hn, dn.cpu().numpy()) and np.array_equal(ho, do.cpu().numpy())
+        W = int(ho[-1])
+        assert np.array_equal(hw, dw.cpu().numpy()[:W])
+
+
+def test_workspace_too_small_is_an_error(mla):
+    import torch
+    from mla_inputs.torch_io import to_device
+    inp = mi.make_config(0)
+    d = to_device(inp, "cuda")
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"],
+                       inp.softmax_scale, num_split=4, workspace=ws)
+    assert e.value.status == -3
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled sequences (all heads) against the oracle
+# ---------------------------------------------------------------------------
+
+def _full(mla, idx, samples, splits=(0,)):
+    import torch
+    from mla_inputs.torch_io import to_device
+    inp = mi.make_config(idx)
+    dev = to_device(inp, "cuda")
+    ref = {b: oracle.mla_decode_ref(inp, batches=[b]) for b in samples}
+    for ns in splits:
+        out, lse = _run(mla, inp, ns, dev)
+        for b in samples:
+            assert_parity(out[b:b + 1], lse[b:b + 1], ref[b][0], ref[b][1], f"config {idx} seq {b} split={ns}")
+    del dev
+    torch.cuda.empty_cache()
+
+
+def test_full_b64_l4096_f16(mla):
+    _full(mla, 1, samples=[0, 21, 63])
+
+
+def test_full_b128_l8192_f16(mla):
+    _full(mla, 2, samples=[0, 127])
+
+
+def test_full_paged_variable_bf16(mla):
+    inp_lens = mi.make_config(3).cache_seqlens
+    longest, shortest = int(np.argmax(inp_lens)), int(np.argmin(inp_lens))
+    _full(mla, 3, samples=sorted({0, longest, shortest}), splits=(0, 4))
+
+
+def test_full_long_context_stress_bf16(mla):
+    _full(mla, 4, samples=[0, 1], splits=(1, 8, 32, 64, 0))

@@ -40,9 +40,9 @@ std::atomic<int32_t> g_num_cus[kMaxDevices];
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: [plan ints][partial lse fp32][partial out fp32].
+// Workspace layout: [plan ints][redo flags][partial lse fp32][partial out fp32].
 struct Layout {
-  size_t num_splits, split_offset, work, part_lse, part_o, total;
+  size_t num_splits, split_offset, work, redo, part_lse, part_o, total;
 };
 
 Layout layout(const mla_desc* d, int32_t max_work) {
@@ -51,7 +51,8 @@ Layout layout(const mla_desc* d, int32_t max_work) {
   L.num_splits = 0;
   L.split_offset = L.num_splits + B * 4;
   L.work = L.split_offset + (B + 1) * 4;
-  L.part_lse = round_up(L.work + 4 * W * 4, 256);
+  L.redo = L.work + 4 * W * 4;
+  L.part_lse = round_up(L.redo + W * 4, 256);
   L.part_o = round_up(L.part_lse + W * H * 4, 256);
   L.total = round_up(L.part_o + W * H * 512 * 4, 256);
   return L;
@@ -274,6 +275,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   int32_t* num_splits = reinterpret_cast<int32_t*>(ws + L.num_splits);
   int32_t* split_offset = reinterpret_cast<int32_t*>(ws + L.split_offset);
   int32_t* work = reinterpret_cast<int32_t*>(ws + L.work);
+  int32_t* redo = reinterpret_cast<int32_t*>(ws + L.redo);
   float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   float* part_o = reinterpret_cast<float*>(ws + L.part_o);
 
@@ -309,6 +311,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.lse = lse;
   sp.part_o = part_o;
   sp.part_lse = part_lse;
+  sp.redo = redo;
   sp.q_nope_sb = d->q_nope_sb;
   sp.q_nope_sh = d->q_nope_sh;
   sp.q_pe_sb = d->q_pe_sb;
@@ -327,8 +330,14 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.num_pages = paged ? d->num_pages : 0;
   sp.row_cap = row_cap;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), stream)) != hipSuccess)
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream)) !=
+      hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
+  // Work items whose main pass overflowed the P range are redone with their
+  // exact max; every other workgroup of this launch exits at once.
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), true, stream)) !=
+      hipSuccess)
+    return fail(MLA_ERR_HIP, "redo launch: %s", hipGetErrorString(e));
   if (ev) (void)hipEventRecord(ev[2], stream);
 
   if (num_split != 1) {

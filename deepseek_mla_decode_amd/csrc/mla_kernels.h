@@ -21,6 +21,7 @@ struct SplitParams {
   float* lse;
   float* part_o;                // [max_work, H, 512]
   float* part_lse;              // [max_work, H], base 2
+  int32_t* redo;                // [max_work]: main pass overflowed, rerun with the exact max
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
   int64_t out_sb, out_sh;
@@ -53,7 +54,8 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream);
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
+                        hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int dtype, int batch, hipStream_t stream);
 
 }  // namespace mla

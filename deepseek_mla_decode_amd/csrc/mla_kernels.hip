@@ -23,19 +23,19 @@
 //   * wave w owns query heads [32w, 32w + 32) of the group; lane l serves head
 //     l % 32 and half g = l / 32 of the contraction slots of every MFMA.
 //   * Scores are formed transposed, Sᵀ[n][h] = K[n][:]·Q[h][:], with
-//     v_mfma_f32_32x32x16: A = 32 cache rows × 16 dims from LDS, B = the wave's
-//     Q slice held in 144 VGPRs for the whole work item.  Each lane then holds
-//     16 scores of ONE head, so max/sum need a single cross-lane step (lane
-//     l ^ 32) and P is already laid out as the B operand of the next product.
+//     v_mfma_f32_32x32x16: A = 32 cache rows × 16 dims read from LDS, B = the
+//     wave's Q slice held in 144 VGPRs for the whole work item.  Each lane then
+//     holds 16 scores of ONE head, so max/sum need a single cross-lane step
+//     (lane l ^ 32) and P is already laid out as the B operand of P·V.
 //   * Output is also transposed, Oᵀ[v][h] += Vᵀ[v][n]·Pᵀ[n][h]: 16 MFMA tiles
 //     of 32 value columns, accumulator 32 heads × 512 fp32 = 256 AGPRs; every
 //     value a lane holds belongs to its own head, so rescaling is lane-local.
-//   * The KV tile (32 rows) is loaded once per workgroup with 128-bit loads,
-//     each wave taking 8 whole rows (one coalesced 1 KiB row per instruction),
-//     and written to LDS twice: row-major [32][576] for the score product and,
-//     after an 8×8 in-register transpose, value-major [512][32] for P·V.
-//     Two LDS buffers of 68 KiB: the next tile's loads are in flight while
-//     the current tile is computed.
+//     The Vᵀ operand is read straight from the row-major tile with gfx950's
+//     transposing LDS read (ds_read_b64_tr_b16): no second copy of the tile.
+//   * Cache rows go HBM -> LDS with global_load_lds_dwordx4 (no VGPRs): one
+//     instruction moves one 1 KiB latent row (or eight 128-byte RoPE rows).
+//     A ring of 4 tiles of 32 rows (36 KiB each) keeps 3 tiles in flight
+//     while one is computed; one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,15 +54,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileRows = 32;                 // cache rows per LDS tile
 constexpr int kThreads = 256;                 // 4 waves
-constexpr int kKChunks = (512 + 64) / 8;      // 16-byte chunks per cache row (72)
-constexpr int kKBytes = kTileRows * kKChunks * 16;   // 36864
-constexpr int kVBytes = 512 * kTileRows * 2;         // 32768
-constexpr int kBufBytes = kKBytes + kVBytes;         // 69632
 constexpr float kLn2 = 0.69314718055994530942f;
-// Lazy rescale threshold (base-2 units): the running max used for the
-// exponentials is only raised when a tile's max exceeds it by more than this,
-// so unnormalised P stays below 2^8.
-constexpr float kRescaleThreshold = 8.0f;
 
 // ---------------------------------------------------------------------------
 // dtype helpers
@@ -79,6 +71,37 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// MFMAs written as inline asm.  The constraint letter pins the accumulator:
+// "v" for the per-tile score tile, "a" for the P·V accumulator, which owns all
+// 256 AGPRs.  (Left to itself the register allocator puts the score tile in
+// AGPRs and pushes part of the P·V accumulator out, and then spills.)  The
+// asm statements also fix the issue order, so the LDS reads below are
+// software-pipelined by hand: an operand is read three MFMAs ahead of use.
+// Hazards the compiler cannot see through asm are covered by explicit
+// s_nop: VALU-written operands before the first MFMA of a group, and MFMA
+// results before VALU reads them.
+template <int DT, bool FIRST>
+__device__ __forceinline__ void mfma_v(f32x16& c, u32x4 a, u32x4 b) {
+  if constexpr (DT == MLA_DTYPE_F16) {
+    if constexpr (FIRST) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  } else {
+    if constexpr (FIRST) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void mfma_a(f32x16& c, u32x4 a, u32x4 b) {
+  if constexpr (DT == MLA_DTYPE_F16) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states after an MFMA result before VALU reads it (>= 18 for the
+// 8-pass 32x32x16 shapes), and after VALU writes before an MFMA reads them.
+__device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+__device__ __forceinline__ void nops_before_mfma() { asm volatile("s_nop 4" ::: "memory"); }
+
 // Round-to-nearest-even fp32 -> 16-bit storage of the input type.
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -94,39 +117,52 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ---------------------------------------------------------------------------
-// LDS addressing (units of 16-byte chunks inside one buffer)
+// LDS tile layout
 // ---------------------------------------------------------------------------
+// One tile = 32 cache rows: a latent region [32][1024 B] followed by a RoPE
+// region [32][128 B].  Inside a row the 16-byte chunk c is stored at slot
+// c ^ swz(n).  With swz(n) = 2(n % 4) + ((n / 4) % 2):
+//   * the score operand read (8 lanes = rows 0..7 of one chunk) and
+//   * the transposing value read (16 lanes = 4 consecutive rows × 2 chunks)
+// both touch 8 distinct 16-byte bank groups.
+constexpr int kLatBytes = kTileRows * 1024;        // 32768
+constexpr int kRopeBytes = kTileRows * 128;        // 4096
+constexpr int kTileBytes = kLatBytes + kRopeBytes; // 36864
+constexpr int kStages = 3;                         // tiles resident in LDS
+constexpr int kQRegSteps = 24;                     // k-steps of Q held in VGPRs; the rest in LDS
+constexpr int kQLdsBytes = (36 - kQRegSteps) * 4 * 1024;
+constexpr int kLoadsPerTile = 9;                   // DMA instructions per wave per tile
 
-// Row-major score operand: row n (0..31), chunk c (0..71; 0..63 latent, 64..71
-// RoPE).  XOR of the chunk index with the row's low bits spreads the 8 rows a
-// group of 8 lanes reads over all banks.
-__device__ __forceinline__ int k_chunk(int n, int c) { return n * kKChunks + (c ^ (n & 7)); }
+__device__ __forceinline__ int swz(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
 
-// Value-major P·V operand: value column v (0..511), chunk c (0..3) of 8
-// positions.  Two columns share a 128-byte line; the XOR mask mixes bits of
-// v so that both the transposing writes (8 lanes -> columns 8 apart) and the
-// MFMA reads (8 lanes -> consecutive columns) hit 8 different 16-byte banks.
-__device__ __forceinline__ int v_chunk(int v, int c) {
-  const int line = v >> 1;
-  const int mask = (line & 3) ^ ((v >> 3) & 7);
-  return kKChunks * kTileRows + line * 8 + (((v & 1) * 4 + c) ^ mask);
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const __attribute__((address_space(1))) void* gptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Position p (0..31) in a value-major column <-> cache row n of the tile.
-// The P·V MFMA's contraction slot (half g, element j) of k-step kt carries row
-// n = 16kt + 8(j/4) + 4g + (j%4) (the layout in which the score MFMA leaves P);
-// storing that row at position p = 16kt + 8g + j makes each lane's operand one
-// contiguous 16-byte chunk.  The map swaps bits 2 and 3.
-__device__ __forceinline__ int pos_to_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+__device__ __forceinline__ u32x4 lds_get16(const lds_char* base, int byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + byte_off);
+}
+
+// Two transposing reads give the 8 contraction values of one A operand.
+__device__ __forceinline__ u32x4 lds_get_tr(const lds_char* base, int off0, int off1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off1));
+  u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
+  return u32x4{a2.x, a2.y, b2.x, b2.y};
+}
 
 // ---------------------------------------------------------------------------
 // Split kernel
 // ---------------------------------------------------------------------------
-
-struct TileRegs {
-  u32x4 lat[8];   // 8 rows x this lane's 16-byte latent chunk
-  u32x4 rope;     // one 16-byte RoPE chunk
-};
 
 // Start of the latent (which == 0) or RoPE (which == 1) part of cache row r;
 // `sel` is the sequence (contiguous) or the physical page (paged).
@@ -137,11 +173,26 @@ __device__ __forceinline__ const uint16_t* row_ptr(const SplitParams& p, int64_t
   return p.kpe + sel * p.kpe_sb + (int64_t)rr * p.kpe_sr;
 }
 
-// Issue the global loads of tile rows [tile_base, tile_base + 32).  Rows at or
-// past r1 are redirected to row r1 - 1 (always valid); their scores are masked.
+// Issue this wave's 9 direct-to-LDS loads of tile rows [tile_base, +32):
+// latent rows 8w..8w+7 and the RoPE parts of the same rows.  Rows at or past
+// r1 are redirected to row r1 - 1 (always valid); their scores are masked.
+// One direct-to-LDS load: 64 lanes x 16 bytes from base + voff (per lane) into
+// the 1 KiB of LDS at lds_addr (lane l -> lds_addr + 16 l).  Issued through
+// inline asm so that the compiler does not add its own conservative waits for
+// the LDS write before every LDS read; the vector-memory counter is managed
+// explicitly by the caller (wait_vmcnt).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(base)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
 template <bool PAGED>
-__device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_base, int r1, int wave,
-                                          int lane, TileRegs& t) {
+__device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_base, int r1, int wave, int lane,
+                                          lds_char* tile) {
+  // `wave`, `tile_base`, `r1` are wave-uniform: row and page arithmetic stays
+  // scalar; only the swizzled 16-byte lane offset is per lane.
   int64_t sel;
   if constexpr (PAGED) {
     const int pg = p.block_table[(int64_t)b * p.bt_stride + tile_base / p.page_size];
@@ -152,65 +203,60 @@ __device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_
   const int last = r1 - 1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int r = tile_base + pos_to_row(8 * wave + i);
+    const int n = 8 * wave + i;          // n % 8 == i
+    int r = tile_base + n;
     r = r < last ? r : last;
-    t.lat[i] = ld16(row_ptr<PAGED>(p, sel, r, 0) + 8 * lane);
+    dma16(row_ptr<PAGED>(p, sel, r, 0), 16u * (uint32_t)(lane ^ swz(i)), lds_u32(tile + n * 1024));
   }
-  const int tid = wave * 64 + lane;
-  int r = tile_base + (tid >> 3);
+  // RoPE: lane l carries row 8w + l/8, chunk l % 8 (stored at slot chunk ^ swz(row)).
+  // The eight rows are not contiguous in memory, so the lane offset is taken
+  // from the first row of the group.
+  const int n0 = 8 * wave;
+  const int n = n0 + (lane >> 3);
+  int r = tile_base + n;
   r = r < last ? r : last;
-  t.rope = ld16(row_ptr<PAGED>(p, sel, r, 1) + 8 * (tid & 7));
+  int rf = tile_base + n0;
+  rf = rf < last ? rf : last;
+  const char* first = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, rf, 1));
+  const char* mine = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, r, 1));
+  dma16(first, (uint32_t)(mine - first) + 16u * (uint32_t)((lane & 7) ^ swz(n)),
+        lds_u32(tile + kLatBytes + n0 * 128));
 }
 
-__device__ __forceinline__ void lds_put(char* base, int byte_off, u32x4 v) {
-  *reinterpret_cast<u32x4*>(base + byte_off) = v;
-}
-__device__ __forceinline__ u32x4 lds_get(const char* base, int byte_off) {
-  return *reinterpret_cast<const u32x4*>(base + byte_off);
-}
-
-// Write a loaded tile into one LDS buffer: row-major copy plus the transposed
-// value-major copy.  Offsets are the closed forms of k_chunk / v_chunk for
-// the rows and columns this lane owns.
-__device__ __forceinline__ void store_tile(char* buf, int wave, int lane, const TileRegs& t) {
+// Q slice of this lane's head: k-step s (dims 16s .. 16s+15, this lane's half
+// g) is the B operand of the score MFMA.  The first kQRegSteps k-steps stay in
+// VGPRs; the rest go to LDS at [step][wave][lane] 16-byte slots.
+__device__ __forceinline__ void load_q(const SplitParams& p, int b, int h, bool head_ok, int wave, int lane,
+                                       lds_char* qlds, u32x4 (&qreg)[kQRegSteps]) {
+  const int g = lane >> 5;
+  const uint16_t* qn = p.q_nope + (int64_t)b * p.q_nope_sb + (int64_t)h * p.q_nope_sh + 8 * g;
+  const uint16_t* qp = p.q_pe + (int64_t)b * p.q_pe_sb + (int64_t)h * p.q_pe_sh + 8 * g;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = pos_to_row(8 * wave + i);
-    lds_put(buf, 16 * k_chunk(n, lane), t.lat[i]);
-  }
-  const int tid = wave * 64 + lane;
-  lds_put(buf, 16 * k_chunk(tid >> 3, 64 + (tid & 7)), t.rope);
-  // 8x8 transpose of 16-bit values: column j of the lane's block (value index
-  // 8*lane + j) across its 8 rows (positions 8*wave .. 8*wave + 7).
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    u32x4 ev, od;
-    ev.x = __builtin_amdgcn_perm(t.lat[1][q], t.lat[0][q], 0x05040100u);
-    ev.y = __builtin_amdgcn_perm(t.lat[3][q], t.lat[2][q], 0x05040100u);
-    ev.z = __builtin_amdgcn_perm(t.lat[5][q], t.lat[4][q], 0x05040100u);
-    ev.w = __builtin_amdgcn_perm(t.lat[7][q], t.lat[6][q], 0x05040100u);
-    od.x = __builtin_amdgcn_perm(t.lat[1][q], t.lat[0][q], 0x07060302u);
-    od.y = __builtin_amdgcn_perm(t.lat[3][q], t.lat[2][q], 0x07060302u);
-    od.z = __builtin_amdgcn_perm(t.lat[5][q], t.lat[4][q], 0x07060302u);
-    od.w = __builtin_amdgcn_perm(t.lat[7][q], t.lat[6][q], 0x07060302u);
-    lds_put(buf, 16 * v_chunk(8 * lane + 2 * q, wave), ev);
-    lds_put(buf, 16 * v_chunk(8 * lane + 2 * q + 1, wave), od);
+  for (int s = 0; s < 36; ++s) {
+    u32x4 v = s < 32 ? ld16(qn + 16 * s) : ld16(qp + 16 * (s - 32));
+    v = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
+    if (s < kQRegSteps) qreg[s < kQRegSteps ? s : 0] = v;
+    else *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(qlds + ((s - kQRegSteps) * 4 + wave) * 1024 + 16 * lane) = v;
   }
 }
 
-template <int DT, bool PAGED>
+// REDO = false: the main pass.  REDO = true: the second launch, which only
+// reruns work items whose main pass flagged an overflow (see below).
+template <int DT, bool PAGED, bool REDO>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kTileBytes + kQLdsBytes];
+  __shared__ int overflow;
+  lds_char* lds = (lds_char*)lds_raw;
+  lds_char* qlds = lds + kStages * kTileBytes;
 
   const int wi = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 31;
   const int g = lane >> 5;
 
-  // ---- work item -----------------------------------------------------------
+  // ---- work item (uniform) -------------------------------------------------
   int b, r0, r1, s_b;
   if (p.num_split > 0) {
     b = wi / p.num_split;
@@ -224,115 +270,178 @@ void split_kernel(SplitParams p) {
     r1 = p.work[4 * wi + 3];
     s_b = p.split_offset[b + 1] - p.split_offset[b];
   }
+  if (REDO && p.redo[wi] == 0) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  r1 = __builtin_amdgcn_readfirstlane(r1);
+  s_b = __builtin_amdgcn_readfirstlane(s_b);
+  const int n_tiles = (r1 - r0 + kTileRows - 1) / kTileRows;
 
-  const int h0 = hg * kHeadsPerGroup + wave * 32;
-  const bool wave_active = h0 < p.heads;
+  // Heads of this wave.  Lanes past the last head compute with a zero query
+  // and write nothing.
+  const int h0 = blockIdx.y * kHeadsPerGroup + wave * 32;
   const bool head_ok = h0 + hl < p.heads;
-  const int h = head_ok ? h0 + hl : p.heads - 1;   // padded lanes read a valid row, then zero it
+  const int h = head_ok ? h0 + hl : p.heads - 1;
 
-  // ---- Q slice: B operand of the score MFMA, k-step s covers dims 16s..16s+15
-  u32x4 qreg[36];
-  {
-    const uint16_t* qn = p.q_nope + (int64_t)b * p.q_nope_sb + (int64_t)h * p.q_nope_sh + 8 * g;
-    const uint16_t* qp = p.q_pe + (int64_t)b * p.q_pe_sb + (int64_t)h * p.q_pe_sh + 8 * g;
+  u32x4 qreg[kQRegSteps];
+  load_q(p, b, h, head_ok, wave, lane, qlds, qreg);
+  if (threadIdx.x == 0) overflow = 0;   // published by the first barrier
+
+  // Per-lane LDS byte offsets inside a tile.
+  // Score operand (row hl, chunk 2s+g): kofs[s % 4] + 128 (s / 4) for s < 32;
+  // RoPE chunk 2(s-32)+g: kofs[s % 4] + rope_delta.
+  const int sw = swz(hl);
+  int kofs[4];
 #pragma unroll
-    for (int s = 0; s < 36; ++s) {
-      const u32x4 v = s < 32 ? ld16(qn + 16 * s) : ld16(qp + 16 * (s - 32));
-      qreg[s] = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < 4; ++i) kofs[i] = hl * 1024 + 16 * ((2 * i + g) ^ sw);
+  const int rope_delta = kLatBytes - hl * 896;
+  // Transposing value reads: 16-lane group G reads rows 16kt + 8r + 4(G/2) + i/4
+  // (i = lane % 16), columns 32vb + 16(G%2) + 4(i%4) .. +3.
+  int vofs[2];
+  {
+    const int i = lane & 15, G = lane >> 4;
+    const int n = 4 * (G >> 1) + (i >> 2);
+    const int f = swz(n);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      vofs[par] = n * 1024 + 16 * ((4 * par + 2 * (G & 1) + ((i >> 1) & 1)) ^ f) + 8 * (i & 1);
   }
+  const int qofs = wave * 1024 + 16 * lane;
 
+  // The exponentials use a reference max `m` that does not change during the
+  // pass over the tiles (changing it would mean rescaling the accumulator,
+  // which must never leave the AGPRs).  The main pass takes m from the first
+  // tile, so P = 2^(x - m) may exceed 1; that is exact while P stays inside the
+  // range of the P·V operand type.  If some tile's max passes m by more than
+  // kOverflowMargin, the main pass writes no output: it flags the work item
+  // and stores the exact max (`mx`, the max over all tiles); the REDO launch
+  // then recomputes the work item with m = mx, where P <= 1.
+  constexpr float kOverflowMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
   f32x16 acc[16];
 #pragma unroll
   for (int vb = 0; vb < 16; ++vb) acc[vb] = f32x16{};
-  float m = -__builtin_inff();   // running max used for the exponentials (base 2, scaled)
-  float lsum = 0.f;              // this lane's share of the running sum
+  float m = REDO ? p.part_lse[(int64_t)wi * p.heads + h] : -__builtin_inff();
+  float mx = -__builtin_inff();   // running max of all tiles seen
+  float lsum = 0.f;               // this lane's share of the sum of P
 
-  // Per-lane LDS byte offsets of the MFMA operands.  Score operand, k-step s:
-  // 16*k_chunk(hl, 2s+g) = kofs[s % 4] + 128*(s / 4).  Value operand, column
-  // block vb, k-step kt: 16*v_chunk(32vb+hl, 2kt+g) = vofs[kt][vb % 2] + 2048*vb.
-  int kofs[4], vofs[2][2];
+  // Prologue: up to three tiles in flight.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kofs[i] = 16 * k_chunk(hl, 2 * i + g);
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    vofs[kt][0] = 16 * v_chunk(hl, 2 * kt + g);
-    vofs[kt][1] = 16 * v_chunk(32 + hl, 2 * kt + g) - 2048;
-  }
-
-  const int n_tiles = (r1 - r0 + kTileRows - 1) / kTileRows;
-  TileRegs tr;
-  if (n_tiles > 0) {
-    load_tile<PAGED>(p, b, r0, r1, wave, lane, tr);
-    store_tile(lds, wave, lane, tr);
-  }
-  __syncthreads();
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < n_tiles) load_tile<PAGED>(p, b, r0 + i * kTileRows, r1, wave, lane, lds + i * kTileBytes);
 
   for (int t = 0; t < n_tiles; ++t) {
     const int tile_base = r0 + t * kTileRows;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile<PAGED>(p, b, tile_base + kTileRows, r1, wave, lane, tr);
+    // Tile t has landed once at most the loads of tiles t+1, t+2 are pending.
+    const int ahead = n_tiles - 1 - t;
+    if (ahead >= 2) wait_vmcnt<2 * kLoadsPerTile>();
+    else if (ahead == 1) wait_vmcnt<kLoadsPerTile>();
+    else wait_vmcnt<0>();
+    // Barrier without a memory fence: the only cross-wave data are the DMA
+    // tiles, whose arrival each wave has just waited for.  The "memory"
+    // clobber keeps LDS reads from moving above it.
+    asm volatile("s_barrier" ::: "memory");
+    if (t + kStages - 1 < n_tiles)
+      load_tile<PAGED>(p, b, tile_base + (kStages - 1) * kTileRows, r1, wave, lane,
+                       lds + ((t + kStages - 1) % kStages) * kTileBytes);
 
-    const char* buf = lds + (t & 1) * kBufBytes;
-    if (wave_active) {
-      // -- scores: Sᵀ[n][h], n = 8(e/4) + 4g + (e%4) for accumulator element e
-      f32x16 sacc = f32x16{};
+    const lds_char* tile = lds + (t % kStages) * kTileBytes;
+    // -- scores: Sᵀ[n][h], n = 8(e/4) + 4g + (e%4) for accumulator element e.
+    //    K operand of k-step s: row hl, chunk 2s+g (RoPE chunks after 32);
+    //    Q operand: VGPRs for s < kQRegSteps, else this wave's LDS slots.
+    f32x16 sacc;
+    {
+      u32x4 kb[5], qb[5];
+      auto kaddr = [&](int s) -> int { return s < 32 ? kofs[s & 3] + 128 * (s >> 2) : kofs[s & 3] + rope_delta; };
 #pragma unroll
-      for (int s = 0; s < 36; ++s) sacc = mfma32<DT>(lds_get(buf + kofs[s & 3], 128 * (s >> 2)), qreg[s], sacc);
-
-      float x[16];
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int n = 8 * (e >> 2) + 4 * g + (e & 3);
-        x[e] = (tile_base + n < r1) ? sacc[e] * p.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[e]);
+      for (int s = 0; s < 3; ++s) {
+        kb[s] = lds_get16(tile, kaddr(s));
+        if (s >= kQRegSteps) qb[s] = lds_get16(qlds, qofs + (s - kQRegSteps) * 4096);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-
-      // -- lazy rescale: only when the tile max passes the used max by > threshold
-      const bool need = tmax > m + kRescaleThreshold;
-      if (__any(need)) {
-        const float mnew = need ? tmax : m;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
-        m = mnew;
-        lsum *= alpha;
 #pragma unroll
-        for (int vb = 0; vb < 16; ++vb) acc[vb] *= alpha;
-      }
-      const float mu = (m == -__builtin_inff()) ? 0.f : m;
-
-      // -- P = 2^(x - m), rounded to the input type: B operand of P·V
-      u32x4 pk[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = __builtin_amdgcn_exp2f(x[8 * kt + j] - mu);
-          lsum += pv[j];
+      for (int s = 0; s < 36; ++s) {
+        if (s + 3 < 36) {
+          kb[(s + 3) % 5] = lds_get16(tile, kaddr(s + 3));
+          if (s + 3 >= kQRegSteps) qb[(s + 3) % 5] = lds_get16(qlds, qofs + (s + 3 - kQRegSteps) * 4096);
         }
-        pk[kt].x = pack2<DT>(pv[0], pv[1]);
-        pk[kt].y = pack2<DT>(pv[2], pv[3]);
-        pk[kt].z = pack2<DT>(pv[4], pv[5]);
-        pk[kt].w = pack2<DT>(pv[6], pv[7]);
+        const u32x4 q = s < kQRegSteps ? qreg[s < kQRegSteps ? s : 0] : qb[s % 5];
+        if (s == 0) mfma_v<DT, true>(sacc, kb[0], q);
+        else mfma_v<DT, false>(sacc, kb[s % 5], q);
       }
+      nops_after_mfma();
+    }
 
-      // -- Oᵀ[v][h] += Vᵀ[v][n] Pᵀ[n][h]
+    float x[16];
+    float tmax = -__builtin_inff();
 #pragma unroll
-      for (int vb = 0; vb < 16; ++vb) {
+    for (int e = 0; e < 16; ++e) {
+      const int n = 8 * (e >> 2) + 4 * g + (e & 3);
+      x[e] = (tile_base + n < r1) ? sacc[e] * p.scale_log2 : -__builtin_inff();
+      tmax = fmaxf(tmax, x[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    mx = fmaxf(mx, tmax);
+    if (!REDO) {
+      if (t == 0) m = tmax;
+      else if (__any(tmax > m + kOverflowMargin) && lane == 0) overflow = 1;
+    }
+    const float mu = (m == -__builtin_inff()) ? 0.f : m;
+
+    // -- P = 2^(x - m) as the B operand of P·V.  fp16: P rounded to fp16.
+    //    bf16: P = hi + lo, both bf16, so the product keeps ~16 bits of P.
+    float pv[16];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          acc[vb] = mfma32<DT>(lds_get(buf + vofs[kt][vb & 1], 2048 * vb), pk[kt], acc[vb]);
+    for (int e = 0; e < 16; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(x[e] - mu);
+      lsum += pv[e];
+    }
+    u32x4 pk[2], pl[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      uint32_t w[4], wl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = pv[8 * kt + 2 * j], cc = pv[8 * kt + 2 * j + 1];
+        w[j] = pack2<DT>(a, cc);
+        if constexpr (DT == MLA_DTYPE_BF16) {
+          const float ah = __builtin_bit_cast(float, w[j] << 16);
+          const float ch = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+          wl[j] = pack2<DT>(a - ah, cc - ch);
         }
+      }
+      pk[kt] = u32x4{w[0], w[1], w[2], w[3]};
+      if constexpr (DT == MLA_DTYPE_BF16) pl[kt] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+    }
+
+    // -- Oᵀ[v][h] += Vᵀ[v][n] Pᵀ[n][h] over 16 blocks of 32 value columns.
+    //    Contraction slot (g, j) of k-step kt is row 16kt + 8(j/4) + 4g + (j%4),
+    //    the layout in which the score MFMA leaves P.  Operand i = 2vb + kt is
+    //    read with two transposing loads, three operands ahead.
+    {
+      auto vaddr = [&](int i) -> int { return vofs[(i >> 1) & 1] + 128 * (i >> 2) + 16384 * (i & 1); };
+      u32x4 vbuf[5];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) vbuf[i] = lds_get_tr(tile + vaddr(i), 0, 8192);
+      nops_before_mfma();
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + 3 < 32) vbuf[(i + 3) % 5] = lds_get_tr(tile + vaddr(i + 3), 0, 8192);
+        mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pk[i & 1]);
+        if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pl[i & 1]);
       }
     }
 
-    if (more) store_tile(lds + ((t + 1) & 1) * kBufBytes, wave, lane, tr);
-    __syncthreads();
   }
-
-  if (!wave_active) return;
+  nops_after_mfma();
+  if (!REDO) {
+    // Every wave's overflow flag write is visible after this barrier.
+    __syncthreads();
+    if (overflow) {
+      if (threadIdx.x == 0) p.redo[wi] = 1;
+      if (head_ok && g == 0) p.part_lse[(int64_t)wi * p.heads + h] = mx;
+      return;
+    }
+    if (threadIdx.x == 0) p.redo[wi] = 0;
+  }
 
   // ---- epilogue: normalise; write final output or the split partial --------
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -340,7 +449,6 @@ void split_kernel(SplitParams p) {
   const float inv = nonempty ? 1.f / ltot : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) + m : -__builtin_inff();
   if (!head_ok) return;
-
   if (s_b == 1) {
     uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh;
 #pragma unroll
@@ -535,16 +643,23 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y,
-                        hipStream_t stream) {
-  const dim3 grid(grid_x, grid_y), block(kThreads);
+template <bool REDO>
+static void launch_split_t(const SplitParams& p, int dtype, bool paged, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
   if (dtype == MLA_DTYPE_F16) {
-    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, false>), grid, block, 0, stream, p);
+    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, true, REDO>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, false, REDO>), grid, block, 0, stream, p);
   } else {
-    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, false>), grid, block, 0, stream, p);
+    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, true, REDO>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, false, REDO>), grid, block, 0, stream, p);
   }
+}
+
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
+                        hipStream_t stream) {
+  const dim3 grid(grid_x, grid_y);
+  if (redo) launch_split_t<true>(p, dtype, paged, grid, stream);
+  else launch_split_t<false>(p, dtype, paged, grid, stream);
   return hipGetLastError();
 }
 

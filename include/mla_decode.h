@@ -131,9 +131,9 @@ int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32
 
 /*
  * Bytes of device workspace mla_decode needs for this description:
- *   plan (int32): B + (B+1) + 4*max_work, rounded to 256 bytes,
- *   partial lse  (fp32, base 2):  max_work * H,
- *   partial out  (fp32):          max_work * H * 512.
+ *   plan (int32): B + (B+1) + 4*max_work, then max_work redo flags, rounded
+ *   to 256 bytes; partial lse (fp32, base 2): max_work * H, rounded to 256;
+ *   partial out (fp32): max_work * H * 512, rounded to 256.
  */
 int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
 
@@ -170,8 +170,11 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *   workspace  device buffer of at least mla_workspace_size() bytes, 256-byte
  *              aligned; its contents on entry do not matter.
  * A sequence with L_b = 0 gets out = 0 and lse = -inf.
- * Launches: planner (planner mode only), split kernel, combine kernel (only
- * touches sequences with s_b > 1; a single split writes out/lse directly).
+ * Launches: planner (planner mode only), split kernel, a second split launch
+ * that only reruns work items whose scores spread beyond the range of P for
+ * the reference max taken from their first tile (all other workgroups exit at
+ * once), and the combine kernel (only touches sequences with s_b > 1; a single
+ * split writes out/lse directly).
  * Calls that share a workspace must be ordered on one stream.
  */
 int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,

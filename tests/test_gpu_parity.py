@@ -217,3 +217,19 @@ def test_full_paged_variable_bf16(mla):
 
 def test_full_long_context_stress_bf16(mla):
     _full(mla, 4, samples=[0, 1], splits=(1, 8, 32, 64, 0))
+
+
+@pytest.mark.parametrize("dtype,boost", [("f16", 30.0), ("bf16", 30.0), ("f16", 5.0), ("f16", 0.5), ("bf16", 2.0)])
+def test_late_dominant_key_reruns_with_exact_max(mla, dtype, boost):
+    """A key far above the first tile's scores (rows 300 and 3000) forces the
+    exact-max rerun when the spread exceeds the P range; moderate boosts do not."""
+    lens = [3100, 400]
+    inp = mi.make_contiguous(2, 128, 3100, lens, dtype, seed=109)
+    one = np.float16(1.0) if dtype == "f16" else mi.f32_to_bf16_bits(np.float32([1.0]))[0]
+    inp.q_pe[:] = one
+    for b, row in ((0, 3000), (1, 300)):
+        inp.k_pe[b, row, 0, :] = mi.cast_storage(np.full(64, boost, dtype=np.float32), dtype)
+    for ns in (0, 1, 3):
+        out, lse = _run(mla, inp, ns)
+        ro, rl = oracle.mla_decode_ref(inp)
+        assert_parity(out, lse, ro, rl, f"dominant key {dtype} boost={boost} split={ns}")

@@ -97,10 +97,23 @@ __device__ __forceinline__ void mfma_a(f32x16& c, u32x4 a, u32x4 b) {
   else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-// Wait states after an MFMA result before VALU reads it (>= 18 for the
-// 8-pass 32x32x16 shapes), and after VALU writes before an MFMA reads them.
-__device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
-__device__ __forceinline__ void nops_before_mfma() { asm volatile("s_nop 4" ::: "memory"); }
+// Wait states between an MFMA writing a register and a VALU instruction
+// reading it (>= 18 for the 16-pass 32x32 shapes), and between VALU writes
+// and an MFMA reading them.  The registers concerned are asm operands, so no
+// read (or write) of them can be scheduled across the s_nop block.
+__device__ __forceinline__ void nops_after_mfma(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(c));
+}
+__device__ __forceinline__ void nops_after_mfma(f32x16 (&acc)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));
+}
+template <int DT>
+__device__ __forceinline__ void nops_before_mfma(u32x4 (&x)[2], u32x4 (&y)[2]) {
+  if constexpr (DT == MLA_DTYPE_F16) asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]));
+  else asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
+}
 
 // Round-to-nearest-even fp32 -> 16-bit storage of the input type.
 template <int DT>
@@ -331,10 +344,10 @@ void split_kernel(SplitParams p) {
 
   for (int t = 0; t < n_tiles; ++t) {
     const int tile_base = r0 + t * kTileRows;
-    // Tile t has landed once at most the loads of tiles t+1, t+2 are pending.
-    const int ahead = n_tiles - 1 - t;
-    if (ahead >= 2) wait_vmcnt<2 * kLoadsPerTile>();
-    else if (ahead == 1) wait_vmcnt<kLoadsPerTile>();
+    // Tile t has landed once only the loads of the tiles after it that are
+    // already issued (at most kStages - 2 of them) are pending.
+    static_assert(kStages == 3, "wait counts below assume a three-tile ring");
+    if (t + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
     else wait_vmcnt<0>();
     // Barrier without a memory fence: the only cross-wave data are the DMA
     // tiles, whose arrival each wave has just waited for.  The "memory"
@@ -367,7 +380,7 @@ void split_kernel(SplitParams p) {
         if (s == 0) mfma_v<DT, true>(sacc, kb[0], q);
         else mfma_v<DT, false>(sacc, kb[s % 5], q);
       }
-      nops_after_mfma();
+      nops_after_mfma(sacc);
     }
 
     float x[16];
@@ -421,7 +434,7 @@ void split_kernel(SplitParams p) {
       u32x4 vbuf[5];
 #pragma unroll
       for (int i = 0; i < 3; ++i) vbuf[i] = lds_get_tr(tile + vaddr(i), 0, 8192);
-      nops_before_mfma();
+      nops_before_mfma<DT>(pk, pl);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         if (i + 3 < 32) vbuf[(i + 3) % 5] = lds_get_tr(tile + vaddr(i + 3), 0, 8192);
@@ -431,7 +444,7 @@ void split_kernel(SplitParams p) {
     }
 
   }
-  nops_after_mfma();
+  nops_after_mfma(acc);
   if (!REDO) {
     // Every wave's overflow flag write is visible after this barrier.
     __syncthreads();

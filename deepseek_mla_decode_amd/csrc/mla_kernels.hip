@@ -115,6 +115,27 @@ __device__ __forceinline__ void nops_before_mfma(u32x4 (&x)[2], u32x4 (&y)[2]) {
   else asm volatile("s_nop 4" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
 }
 
+// Reductions across the two halves of a wave (lane l with lane l ^ 32) through
+// v_permlane32_swap, a VALU op: it exchanges the upper half of its first
+// register with the lower half of its second, so afterwards one register holds
+// this lane's value and the other its partner's, and max / sum of the pair is
+// the same in both halves.  Written as asm with two distinct registers: the
+// builtin, given the same value twice, is folded as if both results were equal.
+// The leading s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
+
 // Round-to-nearest-even fp32 -> 16-bit storage of the input type.
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -133,11 +154,16 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 // LDS tile layout
 // ---------------------------------------------------------------------------
 // One tile = 32 cache rows: a latent region [32][1024 B] followed by a RoPE
-// region [32][128 B].  Inside a row the 16-byte chunk c is stored at slot
-// c ^ swz(n).  With swz(n) = 2(n % 4) + ((n / 4) % 2):
-//   * the score operand read (8 lanes = rows 0..7 of one chunk) and
-//   * the transposing value read (16 lanes = 4 consecutive rows × 2 chunks)
-// both touch 8 distinct 16-byte bank groups.
+// region [32][128 B].  gfx950 serves LDS reads 256 bytes (64 banks) at a time:
+// 16 lanes of a 16-byte read, 32 lanes of an 8-byte read.  Chunks are XOR
+// swizzled so that both operand reads are conflict-free:
+//   latent: 16-byte chunk c of row n at slot c ^ swz_lat(n), swz_lat(n) =
+//     4(n % 4) + (n / 4) % 4, distinct over any 16 consecutive rows (score
+//     operand: 16 rows of one chunk) and mapping 4 consecutive rows onto the
+//     four 4-chunk quarters of a 256-byte line (transposing value read: 4 rows
+//     x 4 chunks);
+//   RoPE (128-byte rows, two per line): chunk c of row n at slot
+//     c ^ ((n / 2) % 8).
 constexpr int kLatBytes = kTileRows * 1024;        // 32768
 constexpr int kRopeBytes = kTileRows * 128;        // 4096
 constexpr int kTileBytes = kLatBytes + kRopeBytes; // 36864
@@ -146,7 +172,8 @@ constexpr int kQRegSteps = 24;                     // k-steps of Q held in VGPRs
 constexpr int kQLdsBytes = (36 - kQRegSteps) * 4 * 1024;
 constexpr int kLoadsPerTile = 9;                   // DMA instructions per wave per tile
 
-__device__ __forceinline__ int swz(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
+__device__ __forceinline__ int swz_lat(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
+__device__ __forceinline__ int swz_rope(int n) { return (n >> 1) & 7; }
 
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -216,12 +243,12 @@ __device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_
   const int last = r1 - 1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int n = 8 * wave + i;          // n % 8 == i
+    const int n = 8 * wave + i;
     int r = tile_base + n;
     r = r < last ? r : last;
-    dma16(row_ptr<PAGED>(p, sel, r, 0), 16u * (uint32_t)(lane ^ swz(i)), lds_u32(tile + n * 1024));
+    dma16(row_ptr<PAGED>(p, sel, r, 0), 16u * (uint32_t)(lane ^ swz_lat(n)), lds_u32(tile + n * 1024));
   }
-  // RoPE: lane l carries row 8w + l/8, chunk l % 8 (stored at slot chunk ^ swz(row)).
+  // RoPE: lane l carries row 8w + l/8, slot l % 8 (holding chunk slot ^ swz_rope(row)).
   // The eight rows are not contiguous in memory, so the lane offset is taken
   // from the first row of the group.
   const int n0 = 8 * wave;
@@ -232,7 +259,7 @@ __device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_
   rf = rf < last ? rf : last;
   const char* first = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, rf, 1));
   const char* mine = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, r, 1));
-  dma16(first, (uint32_t)(mine - first) + 16u * (uint32_t)((lane & 7) ^ swz(n)),
+  dma16(first, (uint32_t)(mine - first) + 16u * (uint32_t)((lane & 7) ^ swz_rope(n)),
         lds_u32(tile + kLatBytes + n0 * 128));
 }
 
@@ -301,23 +328,24 @@ void split_kernel(SplitParams p) {
   if (threadIdx.x == 0) overflow = 0;   // published by the first barrier
 
   // Per-lane LDS byte offsets inside a tile.
-  // Score operand (row hl, chunk 2s+g): kofs[s % 4] + 128 (s / 4) for s < 32;
-  // RoPE chunk 2(s-32)+g: kofs[s % 4] + rope_delta.
-  const int sw = swz(hl);
-  int kofs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kofs[i] = hl * 1024 + 16 * ((2 * i + g) ^ sw);
-  const int rope_delta = kLatBytes - hl * 896;
-  // Transposing value reads: 16-lane group G reads rows 16kt + 8r + 4(G/2) + i/4
-  // (i = lane % 16), columns 32vb + 16(G%2) + 4(i%4) .. +3.
+  //   Score operand, k-step s < 32 (row hl, chunk 2s+g):
+  //     klat + 256 (s / 8) + 16 ((2 (s % 8)) ^ kx), kx = g ^ swz_lat(hl).
+  //   RoPE k-step s >= 32 (chunk 2(s-32)+g): krope + 16 ((2(s-32) + g) ^ swz_rope(hl)).
+  //   Transposing value read for column block vb, k-step kt, half r:
+  //     (vofs[r] ^ 64 (vb % 4)) + 256 (vb / 4) + 16384 kt + 8192 r.
+  const int klat = hl * 1024;
+  const int kx = g ^ swz_lat(hl);
+  const int krope = kLatBytes + hl * 128;
+  const int kxr = swz_rope(hl);
   int vofs[2];
   {
     const int i = lane & 15, G = lane >> 4;
-    const int n = 4 * (G >> 1) + (i >> 2);
-    const int f = swz(n);
+    const int y = 2 * (G & 1) + ((i >> 1) & 1);
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-      vofs[par] = n * 1024 + 16 * ((4 * par + 2 * (G & 1) + ((i >> 1) & 1)) ^ f) + 8 * (i & 1);
+    for (int r = 0; r < 2; ++r) {
+      const int z = (2 * r + (G >> 1)) & 3;
+      vofs[r] = 4096 * (G >> 1) + 1024 * (i >> 2) + 64 * (i >> 2) + 16 * (y ^ z) + 8 * (i & 1);
+    }
   }
   const int qofs = wave * 1024 + 16 * lane;
 
@@ -364,7 +392,9 @@ void split_kernel(SplitParams p) {
     f32x16 sacc;
     {
       u32x4 kb[5], qb[5];
-      auto kaddr = [&](int s) -> int { return s < 32 ? kofs[s & 3] + 128 * (s >> 2) : kofs[s & 3] + rope_delta; };
+      auto kaddr = [&](int s) -> int {
+        return s < 32 ? klat + 256 * (s >> 3) + 16 * ((2 * (s & 7)) ^ kx) : krope + 16 * ((2 * (s - 32) + g) ^ kxr);
+      };
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         kb[s] = lds_get16(tile, kaddr(s));
@@ -384,14 +414,19 @@ void split_kernel(SplitParams p) {
     }
 
     float x[16];
-    float tmax = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int n = 8 * (e >> 2) + 4 * g + (e & 3);
-      x[e] = (tile_base + n < r1) ? sacc[e] * p.scale_log2 : -__builtin_inff();
-      tmax = fmaxf(tmax, x[e]);
+    for (int e = 0; e < 16; ++e) x[e] = sacc[e] * p.scale_log2;
+    if (tile_base + kTileRows > r1) {   // last tile: mask rows at or past r1
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int n = 8 * (e >> 2) + 4 * g + (e & 3);
+        if (tile_base + n >= r1) x[e] = -__builtin_inff();
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    float tmax = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
+    tmax = halves_max(tmax);
     mx = fmaxf(mx, tmax);
     if (!REDO) {
       if (t == 0) m = tmax;
@@ -430,14 +465,18 @@ void split_kernel(SplitParams p) {
     //    the layout in which the score MFMA leaves P.  Operand i = 2vb + kt is
     //    read with two transposing loads, three operands ahead.
     {
-      auto vaddr = [&](int i) -> int { return vofs[(i >> 1) & 1] + 128 * (i >> 2) + 16384 * (i & 1); };
+      // operand i = 2 vb + kt
+      auto vaddr = [&](int i, int r) -> int {
+        const int vb = i >> 1, kt = i & 1;
+        return (vofs[r] ^ (64 * (vb & 3))) + 256 * (vb >> 2) + 16384 * kt + 8192 * r;
+      };
       u32x4 vbuf[5];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) vbuf[i] = lds_get_tr(tile + vaddr(i), 0, 8192);
+      for (int i = 0; i < 3; ++i) vbuf[i] = lds_get_tr(tile, vaddr(i, 0), vaddr(i, 1));
       nops_before_mfma<DT>(pk, pl);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        if (i + 3 < 32) vbuf[(i + 3) % 5] = lds_get_tr(tile + vaddr(i + 3), 0, 8192);
+        if (i + 3 < 32) vbuf[(i + 3) % 5] = lds_get_tr(tile, vaddr(i + 3, 0), vaddr(i + 3, 1));
         mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pk[i & 1]);
         if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pl[i & 1]);
       }
@@ -457,7 +496,7 @@ void split_kernel(SplitParams p) {
   }
 
   // ---- epilogue: normalise; write final output or the split partial --------
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = halves_sum(lsum);
   const bool nonempty = ltot > 0.f;
   const float inv = nonempty ? 1.f / ltot : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) + m : -__builtin_inff();

@@ -230,7 +230,8 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   int st;
   if ((st = check_desc(d)) != MLA_OK) return st;
   if ((st = check_num_split(num_split)) != MLA_OK) return st;
-  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (d->batch == 0) return ok();
   if (!q_nope || !q_pe || !kv_latent || !k_pe || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "NULL data pointer");
@@ -240,6 +241,8 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     if (s < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride %lld", (long long)s);
     if (s % 8) return fail(MLA_ERR_UNSUPPORTED, "stride %lld is not a multiple of 8 elements", (long long)s);
   }
+  if (d->kv_sr >= MLA_MAX_ROW_STRIDE || d->kpe_sr >= MLA_MAX_ROW_STRIDE)
+    return fail(MLA_ERR_UNSUPPORTED, "cache row strides must be below %d elements", MLA_MAX_ROW_STRIDE);
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(kv_latent, 16) || !aligned(k_pe, 16) ||
       !aligned(out, 16))
     return fail(MLA_ERR_UNSUPPORTED, "q/cache/out pointers must be 16-byte aligned");

@@ -34,8 +34,11 @@
 //     transposing LDS read (ds_read_b64_tr_b16): no second copy of the tile.
 //   * Cache rows go HBM -> LDS with global_load_lds_dwordx4 (no VGPRs): one
 //     instruction moves one 1 KiB latent row (or eight 128-byte RoPE rows).
-//     A ring of 4 tiles of 32 rows (36 KiB each) keeps 3 tiles in flight
-//     while one is computed; one barrier per tile.
+//     A ring of 4 tiles of 32 rows (36 KiB each): two tiles in flight, one
+//     being scored, one being multiplied into the output; one barrier per tile.
+//   * One wave per SIMD, so the loop is software-pipelined by hand: the score
+//     MFMAs of tile t run with the softmax of tile t-1 placed between them,
+//     then the P·V MFMAs of tile t-1; LDS operands are read three MFMAs ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -167,105 +170,200 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 constexpr int kLatBytes = kTileRows * 1024;        // 32768
 constexpr int kRopeBytes = kTileRows * 128;        // 4096
 constexpr int kTileBytes = kLatBytes + kRopeBytes; // 36864
-constexpr int kStages = 3;                         // tiles resident in LDS
-constexpr int kQRegSteps = 24;                     // k-steps of Q held in VGPRs; the rest in LDS
-constexpr int kQLdsBytes = (36 - kQRegSteps) * 4 * 1024;
+constexpr int kStages = 4;                         // LDS ring of tiles (144 KiB)
 constexpr int kLoadsPerTile = 9;                   // DMA instructions per wave per tile
+constexpr int kQRegSteps = 32;                     // Q k-steps held in VGPRs (the latent part)
+constexpr int kQLdsBytes = 4 * 4 * 1024;           // RoPE k-steps of Q: [step][wave][lane] x 16 B
+static_assert(kStages * kTileBytes + kQLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
 __device__ __forceinline__ int swz_lat(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int n) { return (n >> 1) & 7; }
 
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) char lds_char;
-typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+// s_waitcnt on the vector-memory counter (VM) and the LDS/scalar-memory
+// counter (LGKM, 15 = no constraint); gfx9 encoding.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (LGKM << 8));
 }
+
+// Barrier without a memory fence: cross-wave data in the loop are DMA tiles,
+// whose arrival every wave waits for explicitly before it.  The "memory"
+// clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Fence for the instruction scheduler: nothing moves across it.  The loop
+// below places one MFMA per fenced region together with the LDS reads and the
+// softmax instructions that are to run while that MFMA occupies the matrix
+// core; a wave per SIMD has no other wave to hide its latencies.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ u32x4 lds_get16(const lds_char* base, int byte_off) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + byte_off);
 }
 
 // Two transposing reads give the 8 contraction values of one A operand.
-__device__ __forceinline__ u32x4 lds_get_tr(const lds_char* base, int off0, int off1) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(base + off0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(base + off1));
+__device__ __forceinline__ u32x4 lds_get_tr(const lds_char* b0, int off0, const lds_char* b1, int off1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(b0 + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(b1 + off1));
   u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
   return u32x4{a2.x, a2.y, b2.x, b2.y};
+}
+
+// max of three floats in one VALU op (fmaxf would first canonicalise each
+// input, as the compiler cannot see that the scores are not signalling NaNs).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // ---------------------------------------------------------------------------
 // Split kernel
 // ---------------------------------------------------------------------------
 
-// Start of the latent (which == 0) or RoPE (which == 1) part of cache row r;
-// `sel` is the sequence (contiguous) or the physical page (paged).
-template <bool PAGED>
-__device__ __forceinline__ const uint16_t* row_ptr(const SplitParams& p, int64_t sel, int r, int which) {
-  const int rr = PAGED ? (r % p.page_size) : r;
-  if (which == 0) return p.kv + sel * p.kv_sb + (int64_t)rr * p.kv_sr;
-  return p.kpe + sel * p.kpe_sb + (int64_t)rr * p.kpe_sr;
+// One direct-to-LDS load: 64 lanes x 16 bytes from base + (lane16 ^ key)
+// (per lane) into the 1 KiB of LDS at lds_addr (lane l -> lds_addr + 16 l).
+// Issued through inline asm so that the compiler does not add its own
+// conservative waits for the LDS write before every LDS read; the
+// vector-memory counter is managed explicitly (wait_cnt).  The lane offset is
+// formed inside the asm so that it cannot be hoisted out of the loop into a
+// register of its own.  One wait state separates the M0 write from the load
+// that reads it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t lane16, uint32_t key, uint32_t lds_addr) {
+  uint32_t voff;
+  asm volatile("v_xor_b32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
+               : "=&v"(voff)
+               : "s"(key), "v"(lane16), "s"(lds_addr), "s"(base)
+               : "memory");
 }
 
-// Issue this wave's 9 direct-to-LDS loads of tile rows [tile_base, +32):
-// latent rows 8w..8w+7 and the RoPE parts of the same rows.  Rows at or past
-// r1 are redirected to row r1 - 1 (always valid); their scores are masked.
-// One direct-to-LDS load: 64 lanes x 16 bytes from base + voff (per lane) into
-// the 1 KiB of LDS at lds_addr (lane l -> lds_addr + 16 l).  Issued through
-// inline asm so that the compiler does not add its own conservative waits for
-// the LDS write before every LDS read; the vector-memory counter is managed
-// explicitly by the caller (wait_vmcnt).
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(base)
-               : "memory");
+// The RoPE load of a tile: lane l carries 16 bytes of row n = 8w + l/8
+// (clamped to nlast) at slot (l % 8) ^ swz_rope(n), from base + nn*rb +
+// 16 ((l % 8) ^ ((n / 2) % 8)) into lds_addr + 16 l.  Everything per lane is
+// formed inside the asm from the lane id (v_mbcnt), for the reason given
+// above and to hold no register across the loop.  w8 = 8w.
+__device__ __forceinline__ void dma16_rope(const void* base, int w8, int nlast, uint32_t rb, uint32_t lds_addr) {
+  uint32_t l, n, t;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 %0, -1, %0\n\t"       // l = lane id
+      "v_lshrrev_b32 %1, 3, %0\n\t"
+      "v_add_u32 %1, %3, %1\n\t"                // n = 8w + l/8
+      "v_lshrrev_b32 %2, 1, %1\n\t"
+      "v_xor_b32 %2, %2, %0\n\t"
+      "v_and_b32 %2, 7, %2\n\t"
+      "v_lshlrev_b32 %2, 4, %2\n\t"             // t = 16 ((l ^ n/2) % 8)
+      "v_min_i32 %1, %4, %1\n\t"
+      "v_mad_u32_u24 %1, %1, %5, %2\n\t"        // nn*rb + t (nn < 32, rb < 2^24)
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %7"
+      : "=&v"(l), "=&v"(n), "=&v"(t)
+      : "s"(w8), "s"(nlast), "s"(rb), "s"(lds_addr), "s"(base)
+      : "memory");
+}
+
+// sbase + (lane_bits ^ key): per-tile LDS read addresses (sbase = the tile's
+// slot, lane_bits = this lane's loop-invariant offset bits, key = the part
+// that varies with the operand).  asm volatile keeps the compiler from
+// hoisting one register per operand offset out of the loop.
+__device__ __forceinline__ uint32_t xor_add(uint32_t sbase, uint32_t key, uint32_t lane_bits) {
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, %1, %2\n\tv_add_u32 %0, %3, %0" : "=&v"(r) : "s"(key), "v"(lane_bits), "s"(sbase));
+  return r;
+}
+
+__device__ __forceinline__ const lds_char* lds_at(uint32_t addr) {
+  return (const lds_char*)(uintptr_t)addr;
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
-template <bool PAGED>
-__device__ __forceinline__ void load_tile(const SplitParams& p, int b, int tile_base, int r1, int wave, int lane,
-                                          lds_char* tile) {
-  // `wave`, `tile_base`, `r1` are wave-uniform: row and page arithmetic stays
-  // scalar; only the swizzled 16-byte lane offset is per lane.
-  int64_t sel;
-  if constexpr (PAGED) {
-    const int pg = p.block_table[(int64_t)b * p.bt_stride + tile_base / p.page_size];
-    sel = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
-  } else {
-    sel = b;
-  }
-  const int last = r1 - 1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = 8 * wave + i;
-    int r = tile_base + n;
-    r = r < last ? r : last;
-    dma16(row_ptr<PAGED>(p, sel, r, 0), 16u * (uint32_t)(lane ^ swz_lat(n)), lds_u32(tile + n * 1024));
-  }
-  // RoPE: lane l carries row 8w + l/8, slot l % 8 (holding chunk slot ^ swz_rope(row)).
-  // The eight rows are not contiguous in memory, so the lane offset is taken
-  // from the first row of the group.
-  const int n0 = 8 * wave;
-  const int n = n0 + (lane >> 3);
-  int r = tile_base + n;
-  r = r < last ? r : last;
-  int rf = tile_base + n0;
-  rf = rf < last ? rf : last;
-  const char* first = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, rf, 1));
-  const char* mine = reinterpret_cast<const char*>(row_ptr<PAGED>(p, sel, r, 1));
-  dma16(first, (uint32_t)(mine - first) + 16u * (uint32_t)((lane & 7) ^ swz_rope(n)),
-        lds_u32(tile + kLatBytes + n0 * 128));
+// Where the work item's cache rows live, and the next tile to load (all
+// wave-uniform).  Tiles are loaded in order, 32 rows apart; a tile (32 rows at
+// a multiple of 32) never straddles a page, since pages hold a multiple of 32
+// rows, so a paged tile is one page index plus a row offset inside the page.
+struct DmaCursor {
+  const char* lat;      // contiguous: latent row `row`; paged: the pool
+  const char* rope;     // likewise for the RoPE part
+  const_i32_ptr bt;     // paged: the block-table entry of the next tile
+  int64_t lat_pb, rope_pb;    // paged: page strides in bytes
+  uint32_t lat_rb, rope_rb;   // row strides in bytes
+  int page_size, num_pages;
+  int row;                    // first logical row of the next tile
+  int in_page;                // paged: its row inside the page
+};
+
+// Physical page of the cursor's tile (paged), clamped to the pool.  A scalar
+// load: the block table is read-only for the kernel.
+__device__ __forceinline__ int cursor_page(const DmaCursor& c) {
+  const int pg = *c.bt;
+  return pg < 0 ? 0 : (pg >= c.num_pages ? c.num_pages - 1 : pg);
 }
 
-// Q slice of this lane's head: k-step s (dims 16s .. 16s+15, this lane's half
-// g) is the B operand of the score MFMA.  The first kQRegSteps k-steps stay in
-// VGPRs; the rest go to LDS at [step][wave][lane] 16-byte slots.
+// One tile's load: base of its row 0 (latent and RoPE) and its last valid row.
+struct DmaTile {
+  const char* lat;
+  const char* rope;
+  int nlast;            // rows at or past it re-read it (0 <= nlast)
+  uint32_t lds;         // the tile's LDS slot
+};
+
+template <bool PAGED>
+__device__ __forceinline__ DmaTile cursor_tile(const DmaCursor& c, int page, int r1, const lds_char* tile) {
+  DmaTile d;
+  if constexpr (PAGED) {
+    d.lat = c.lat + page * c.lat_pb + (int64_t)c.in_page * c.lat_rb;
+    d.rope = c.rope + page * c.rope_pb + (int64_t)c.in_page * c.rope_rb;
+  } else {
+    d.lat = c.lat;
+    d.rope = c.rope;
+  }
+  d.nlast = r1 - 1 - c.row;
+  d.lds = lds_u32(tile);
+  return d;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ void cursor_next(DmaCursor& c) {
+  c.row += kTileRows;
+  if constexpr (PAGED) {
+    // Branch-free (a branch here splits the loop body and costs register
+    // copies at the join).
+    c.in_page += kTileRows;
+    const int wrap = c.in_page == c.page_size ? 1 : 0;
+    c.in_page -= wrap * c.page_size;
+    c.bt += wrap;
+  } else {
+    c.lat += (int64_t)kTileRows * c.lat_rb;
+    c.rope += (int64_t)kTileRows * c.rope_rb;
+  }
+}
+
+// This wave's part of a tile load: part 0 moves the RoPE parts of rows
+// 8w .. 8w+7 (first, so that its base register is free early), part i >= 1
+// latent row 8w + i - 1.  Rows past nlast re-read row nlast (always valid);
+// their scores are masked.
+__device__ __forceinline__ void issue_part(const DmaCursor& c, const DmaTile& d, int wave, uint32_t lane16,
+                                           int part) {
+  if (part > 0) {
+    const int n = 8 * wave + part - 1;
+    const int nn = n < d.nlast ? n : d.nlast;
+    dma16(d.lat + (uint32_t)nn * c.lat_rb, lane16, (uint32_t)(16 * swz_lat(n)), d.lds + n * 1024);
+  } else {
+    // lane l carries row 8w + l/8, slot l % 8 (holding chunk slot ^ swz_rope(row))
+    dma16_rope(d.rope, 8 * wave, d.nlast, c.rope_rb, d.lds + kLatBytes + 8 * wave * 128);
+  }
+}
+
+// Q slice of this lane's head: k-step s (dims 16s .. 16s+15, half g of them)
+// is the B operand of the score MFMA.  The 32 latent k-steps stay in VGPRs
+// for the whole work item; the 4 RoPE k-steps go to this wave's LDS slots
+// (16 bytes per lane, [step][wave][lane]).
 __device__ __forceinline__ void load_q(const SplitParams& p, int b, int h, bool head_ok, int wave, int lane,
                                        lds_char* qlds, u32x4 (&qreg)[kQRegSteps]) {
   const int g = lane >> 5;
@@ -276,17 +374,85 @@ __device__ __forceinline__ void load_q(const SplitParams& p, int b, int h, bool 
     u32x4 v = s < 32 ? ld16(qn + 16 * s) : ld16(qp + 16 * (s - 32));
     v = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
     if (s < kQRegSteps) qreg[s < kQRegSteps ? s : 0] = v;
-    else *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(qlds + ((s - kQRegSteps) * 4 + wave) * 1024 + 16 * lane) = v;
+    else *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(qlds + (((s - kQRegSteps) * 4 + wave) * 64 + lane) * 16) = v;
   }
 }
 
+// Softmax of one score tile, cut into steps so that the loop can run them one
+// or two instructions at a time between MFMAs.  x[] holds the raw scores
+// (q·k, not yet scaled) of this lane's head; the steps turn them into
+// P = 2^(c x - c m) and pack P as the B operand of P·V.  c = softmax_scale ·
+// log2(e) > 0, so the max of the raw scores is the max of the scaled ones.
+//
+// The reference max `m` does not change during the pass over the tiles
+// (changing it would mean rescaling the accumulator, which must never leave
+// the AGPRs).  The main pass takes m from the first tile, so P may exceed 1;
+// that is exact while P stays inside the range of the P·V operand type.  If
+// some tile's max passes m by more than the margin, the main pass writes no
+// output: it flags the work item and stores the exact max (`mx`, the max over
+// all tiles); the REDO launch then recomputes the work item with m = mx.
+template <int DT, bool REDO>
+struct Softmax {
+  float x[16];
+  float t0, t1, t2, t3, t4, tmax;
+  u32x4 pk[2], pl[2];   // P packed (bf16: high part in pk, low part in pl)
+
+  // Step `s` (0..22).  `first`: this is the work item's first tile, which
+  // fixes m; only nmc = -c m is kept.  mx tracks the max over all tiles.
+  __device__ __forceinline__ void step(int s, bool first, float c, float& nmc, float& mx, float& lsum) {
+    if (s == 0) { t0 = max3(x[0], x[1], x[2]); t1 = max3(x[3], x[4], x[5]); }
+    if (s == 1) { t2 = max3(x[6], x[7], x[8]); t3 = max3(x[9], x[10], x[11]); }
+    if (s == 2) { t4 = max3(x[12], x[13], x[14]); t0 = max3(t0, t1, x[15]); }
+    if (s == 3) { tmax = max3(t0, t2, t3); tmax = max3(tmax, t4, t4); }
+    if (s == 4) {
+      float a = tmax, b = tmax;
+      swap_halves(a, b);
+      tmax = max3(a, b, b);
+    }
+    if (s == 5) {
+      mx = max3(mx, tmax, tmax);
+      if (!REDO && first) nmc = -(tmax * c);
+    }
+    if (s >= 6 && s < 22) {
+      const int e = s - 6;
+      x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, nmc));
+    }
+    if (s >= 7 && s < 23) lsum += x[s - 7];
+    if (s >= 8 && s < 23 && (s & 1) == 0) {
+      const int j = (s - 8) >> 1;   // pair j = exponentials 2j, 2j+1
+      const float a = x[2 * j], bb = x[2 * j + 1];
+      const uint32_t w = pack2<DT>(a, bb);
+      pk[j >> 2][j & 3] = w;
+      if constexpr (DT == MLA_DTYPE_BF16) {
+        const float ah = __builtin_bit_cast(float, w << 16);
+        const float bh = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        pl[j >> 2][j & 3] = pack2<DT>(a - ah, bb - bh);
+      }
+    }
+  }
+};
+constexpr int kSoftmaxSteps = 23;
+
 // REDO = false: the main pass.  REDO = true: the second launch, which only
-// reruns work items whose main pass flagged an overflow (see below).
+// reruns work items whose main pass flagged an overflow.
+//
+// Schedule (one wave, work item of n tiles; tile t in LDS slot t % 4):
+//   prologue   DMA tiles 0, 1, 2; wait for tile 0; barrier
+//   step t     A: the 36 score MFMAs of tile t, with the softmax of tile t-1
+//                 run between them (steps of Softmax), K reads ahead;
+//              B: the P·V MFMAs of tile t-1, V reads ahead, and this wave's
+//                 9 loads of tile t+2 (into tile t-2's slot), one every three
+//                 MFMAs;
+//              before its last few MFMAs: wait until tile t+1 has landed and
+//                 every wave has finished reading tile t-1, then start the K
+//                 reads of tile t+1.
+//   drain      softmax of tile n-1 (masked), P·V of tile n-1.
+// Two tiles stay in flight, one barrier per tile; only the last tile can be
+// partial, so masking is confined to the drain.
 template <int DT, bool PAGED, bool REDO>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kTileBytes + kQLdsBytes];
-  __shared__ int overflow;
   lds_char* lds = (lds_char*)lds_raw;
   lds_char* qlds = lds + kStages * kTileBytes;
 
@@ -295,6 +461,7 @@ void split_kernel(SplitParams p) {
   const int lane = threadIdx.x & 63;
   const int hl = lane & 31;
   const int g = lane >> 5;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
 
   // ---- work item (uniform) -------------------------------------------------
   int b, r0, r1, s_b;
@@ -325,168 +492,267 @@ void split_kernel(SplitParams p) {
 
   u32x4 qreg[kQRegSteps];
   load_q(p, b, h, head_ok, wave, lane, qlds, qreg);
-  if (threadIdx.x == 0) overflow = 0;   // published by the first barrier
+  // This wave's Q RoPE slots: qlds + 1024 wave + 16 lane (+ 4096 per k-step).
+  const uint32_t qwave = lds_u32(qlds) + 1024u * (uint32_t)wave;
 
-  // Per-lane LDS byte offsets inside a tile.
-  //   Score operand, k-step s < 32 (row hl, chunk 2s+g):
-  //     klat + 256 (s / 8) + 16 ((2 (s % 8)) ^ kx), kx = g ^ swz_lat(hl).
-  //   RoPE k-step s >= 32 (chunk 2(s-32)+g): krope + 16 ((2(s-32) + g) ^ swz_rope(hl)).
-  //   Transposing value read for column block vb, k-step kt, half r:
-  //     (vofs[r] ^ 64 (vb % 4)) + 256 (vb / 4) + 16384 kt + 8192 r.
-  const int klat = hl * 1024;
-  const int kx = g ^ swz_lat(hl);
-  const int krope = kLatBytes + hl * 128;
-  const int kxr = swz_rope(hl);
-  int vofs[2];
+  DmaCursor cur;
+  cur.lat_rb = (uint32_t)(p.kv_sr * 2);
+  cur.rope_rb = (uint32_t)(p.kpe_sr * 2);
+  cur.row = r0;
+  if constexpr (PAGED) {
+    cur.lat = reinterpret_cast<const char*>(p.kv);
+    cur.rope = reinterpret_cast<const char*>(p.kpe);
+    const int slot0 = r0 / p.page_size;
+    cur.bt = (const_i32_ptr)(p.block_table + (int64_t)b * p.bt_stride + slot0);
+    cur.lat_pb = p.kv_sb * 2;
+    cur.rope_pb = p.kpe_sb * 2;
+    cur.page_size = p.page_size;
+    cur.num_pages = p.num_pages;
+    cur.in_page = r0 - slot0 * p.page_size;
+  } else {
+    cur.lat = reinterpret_cast<const char*>(p.kv + (int64_t)b * p.kv_sb) + (int64_t)r0 * cur.lat_rb;
+    cur.rope = reinterpret_cast<const char*>(p.kpe + (int64_t)b * p.kpe_sb) + (int64_t)r0 * cur.rope_rb;
+  }
+
+  // LDS byte offsets inside a tile, as loop-invariant lane bits plus a key
+  // (disjoint bit ranges, so xor and add agree):
+  //   score operand, k-step s < 32 (row hl, chunk 2s + g):
+  //     hl*1024 + 256 (s / 8) + 16 ((2 (s % 8)) ^ kx), kx = g ^ swz_lat(hl)
+  //     = (klx ^ 32 (s % 8)) + 256 (s / 8),   klx = hl*1024 | 16 kx;
+  //   RoPE k-step 32 + u (chunk 2u + g):
+  //     kLatBytes + hl*128 + 16 ((2u + g) ^ swz_rope(hl)) = rkx ^ 32u;
+  //   transposing value read for column block vb, k-step kt, half r:
+  //     (vofs0 ^ 32 r ^ 64 (vb % 4)) + 256 (vb / 4) + 16384 kt + 8192 r.
+  const uint32_t klx = (uint32_t)(hl * 1024) | (uint32_t)(16 * (g ^ swz_lat(hl)));
+  const uint32_t rkx = (uint32_t)(kLatBytes + hl * 128) | (uint32_t)(16 * (g ^ swz_rope(hl)));
+  // vofs1 = vofs0 ^ 32: the two halves differ only in z's bit 1.
+  uint32_t vofs0;
   {
     const int i = lane & 15, G = lane >> 4;
     const int y = 2 * (G & 1) + ((i >> 1) & 1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int z = (2 * r + (G >> 1)) & 3;
-      vofs[r] = 4096 * (G >> 1) + 1024 * (i >> 2) + 64 * (i >> 2) + 16 * (y ^ z) + 8 * (i & 1);
-    }
+    const int z = (G >> 1) & 3;
+    vofs0 = 4096 * (G >> 1) + 1024 * (i >> 2) + 64 * (i >> 2) + 16 * (y ^ z) + 8 * (i & 1);
   }
-  const int qofs = wave * 1024 + 16 * lane;
+  auto slot = [&](int t) __attribute__((always_inline)) -> lds_char* { return lds + (t & (kStages - 1)) * kTileBytes; };
 
-  // The exponentials use a reference max `m` that does not change during the
-  // pass over the tiles (changing it would mean rescaling the accumulator,
-  // which must never leave the AGPRs).  The main pass takes m from the first
-  // tile, so P = 2^(x - m) may exceed 1; that is exact while P stays inside the
-  // range of the P·V operand type.  If some tile's max passes m by more than
-  // kOverflowMargin, the main pass writes no output: it flags the work item
-  // and stores the exact max (`mx`, the max over all tiles); the REDO launch
-  // then recomputes the work item with m = mx, where P <= 1.
-  constexpr float kOverflowMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
+  const float c = p.scale_log2;
+
+  // An empty work item (more splits than blocks, or L = 0) writes out = 0 /
+  // lse = -inf (or a zero partial, lse = -inf) and leaves before the
+  // accumulator exists, so that it has a single definition path.
+  if (n_tiles == 0) {
+    if (!REDO && threadIdx.x == 0) p.redo[wi] = 0;
+    if (REDO || !head_ok) return;
+    if (s_b == 1) {
+      uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 4 * g;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
+      if (g == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
+    } else {
+      float* o = p.part_o + ((int64_t)wi * p.heads + h) * 512 + 4 * g;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) *reinterpret_cast<f32x4*>(o + 8 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g == 0) p.part_lse[(int64_t)wi * p.heads + h] = -__builtin_inff();
+    }
+    return;
+  }
+
   f32x16 acc[16];
 #pragma unroll
   for (int vb = 0; vb < 16; ++vb) acc[vb] = f32x16{};
-  float m = REDO ? p.part_lse[(int64_t)wi * p.heads + h] : -__builtin_inff();
-  float mx = -__builtin_inff();   // running max of all tiles seen
+  // Reference max m (raw-score units): the REDO launch reads it, the main
+  // pass takes it from the first tile.
+  float nmc = REDO ? -(p.part_lse[(int64_t)wi * p.heads + h] * c) : 0.f;
+  float mx = -__builtin_inff();   // running max of all tiles seen (raw)
   float lsum = 0.f;               // this lane's share of the sum of P
 
-  // Prologue: up to three tiles in flight.
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < n_tiles) load_tile<PAGED>(p, b, r0 + i * kTileRows, r1, wave, lane, lds + i * kTileBytes);
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int tile_base = r0 + t * kTileRows;
-    // Tile t has landed once only the loads of the tiles after it that are
-    // already issued (at most kStages - 2 of them) are pending.
-    static_assert(kStages == 3, "wait counts below assume a three-tile ring");
-    if (t + 1 < n_tiles) wait_vmcnt<kLoadsPerTile>();
-    else wait_vmcnt<0>();
-    // Barrier without a memory fence: the only cross-wave data are the DMA
-    // tiles, whose arrival each wave has just waited for.  The "memory"
-    // clobber keeps LDS reads from moving above it.
-    asm volatile("s_barrier" ::: "memory");
-    if (t + kStages - 1 < n_tiles)
-      load_tile<PAGED>(p, b, tile_base + (kStages - 1) * kTileRows, r1, wave, lane,
-                       lds + ((t + kStages - 1) % kStages) * kTileBytes);
-
-    const lds_char* tile = lds + (t % kStages) * kTileBytes;
-    // -- scores: Sᵀ[n][h], n = 8(e/4) + 4g + (e%4) for accumulator element e.
-    //    K operand of k-step s: row hl, chunk 2s+g (RoPE chunks after 32);
-    //    Q operand: VGPRs for s < kQRegSteps, else this wave's LDS slots.
-    f32x16 sacc;
+  {
+    // ---- prologue ----------------------------------------------------------
     {
-      u32x4 kb[5], qb[5];
-      auto kaddr = [&](int s) -> int {
-        return s < 32 ? klat + 256 * (s >> 3) + 16 * ((2 * (s & 7)) ^ kx) : krope + 16 * ((2 * (s - 32) + g) ^ kxr);
-      };
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        kb[s] = lds_get16(tile, kaddr(s));
-        if (s >= kQRegSteps) qb[s] = lds_get16(qlds, qofs + (s - kQRegSteps) * 4096);
+      for (int k = 0; k < 3; ++k) {
+        if (k < n_tiles) {
+          const int pg = PAGED ? cursor_page(cur) : 0;
+          const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(k));
+#pragma unroll
+          for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+          cursor_next<PAGED>(cur);
+        }
+      }
+      if (n_tiles > 2) wait_cnt<2 * kLoadsPerTile, 15>();
+      else if (n_tiles > 1) wait_cnt<kLoadsPerTile, 15>();
+      else wait_cnt<0, 15>();
+      barrier();
+    }
+
+    // LDS operands are read kKA (score) / kVA (value) MFMAs ahead, as far as
+    // the registers allow: value operands three ahead for fp16, two for bf16
+    // (whose split P takes the registers).  Ring sizes: read-ahead + the
+    // operand in use (an MFMA has taken its A and B operands once it issues).
+    constexpr int kKA = 2;
+    constexpr int kVA = DT == MLA_DTYPE_F16 ? 3 : 2;
+    constexpr int kKB = kKA + 1, kVB = kVA + 1;
+    u32x4 kb[kKB], vbuf[kVB], qb[4];
+    uint32_t kq[8], vw[2][4];
+    f32x16 sA, sB;
+    Softmax<DT, REDO> sm;
+
+    // Score-operand bases of a tile, then its first kKA K reads.
+    auto k_head = [&](const lds_char* tile) __attribute__((always_inline)) {
+      const uint32_t base = lds_u32(tile);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kq[j] = xor_add(base, 32u * j, klx);
+#pragma unroll
+      for (int s = 0; s < kKA; ++s) kb[s] = lds_get16(lds_at(kq[s]), 0);
+    };
+    auto k_read = [&](const lds_char* tile, int s) __attribute__((always_inline)) -> u32x4 {
+      if (s < 32) return lds_get16(lds_at(kq[s & 7]), 256 * (s >> 3));
+      return lds_get16(lds_at(xor_add(lds_u32(tile), 32u * (s - 32), rkx)), 0);
+    };
+    // B operand of score step s: Q in VGPRs, or the RoPE part read from LDS.
+    auto q_op = [&](int s) __attribute__((always_inline)) -> const u32x4& {
+      return s < kQRegSteps ? qreg[s < kQRegSteps ? s : 0] : qb[s < kQRegSteps ? 0 : s - kQRegSteps];
+    };
+    // Value-operand bases of a tile; operand i = 2 vb + kt, two reads.
+    auto v_bases = [&](const lds_char* tile) __attribute__((always_inline)) {
+      const uint32_t base = lds_u32(tile);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) vw[r][cc] = xor_add(base, 64u * cc + 32u * r, vofs0);
+    };
+    auto v_read = [&](int i) __attribute__((always_inline)) -> u32x4 {
+      const int vb = i >> 1, kt = i & 1;
+      const int imm = 256 * (vb >> 2) + 16384 * kt;
+      return lds_get_tr(lds_at(vw[0][vb & 3]), imm, lds_at(vw[1][vb & 3]), imm + 8192);
+    };
+    // Score MFMAs of one tile into `sc`; with WITH_SM, the softmax of the
+    // previous tile runs between them and the first kVA V reads of the
+    // previous tile are issued at the end.
+    // With WITH_DMA, this wave's loads of tile dma_t (page dma_pg) are issued
+    // one every four MFMAs, wave w in the slots s = w (mod 4): the CU's
+    // vector-memory path takes a 1 KiB load every dozen or so cycles, and
+    // loads issued together (by one wave, or by the four waves at once) stall
+    // the issuing wave, and with it its MFMAs.
+    auto phase_a = [&](const lds_char* tile, f32x16& sc, f32x16& prev, bool with_sm, bool first_prev,
+                       const lds_char* vtile) __attribute__((always_inline)) {
+      if (with_sm) {
+        // Tile 0's scores come straight from its MFMAs: pad the hazard.
+        if (first_prev) nops_after_mfma(prev);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sm.x[e] = prev[e];
       }
 #pragma unroll
       for (int s = 0; s < 36; ++s) {
-        if (s + 3 < 36) {
-          kb[(s + 3) % 5] = lds_get16(tile, kaddr(s + 3));
-          if (s + 3 >= kQRegSteps) qb[(s + 3) % 5] = lds_get16(qlds, qofs + (s + 3 - kQRegSteps) * 4096);
+        if (s == 0) mfma_v<DT, true>(sc, kb[0], qreg[0]);
+        else mfma_v<DT, false>(sc, kb[s % kKB], q_op(s));
+        if (s + kKA < 36) kb[(s + kKA) % kKB] = k_read(tile, s + kKA);
+        if (s + kKA >= kQRegSteps && s + kKA < 36)
+          qb[s + kKA - kQRegSteps] = lds_get16(lds_at(xor_add(qwave, 0u, lane16)), (s + kKA - kQRegSteps) * 4096);
+        if (with_sm) {
+          if (s < kSoftmaxSteps) sm.step(s, first_prev, c, nmc, mx, lsum);
+          if (s == 30) v_bases(vtile);
+          if (s >= 36 - kVA) vbuf[s - (36 - kVA)] = v_read(s - (36 - kVA));
         }
-        const u32x4 q = s < kQRegSteps ? qreg[s < kQRegSteps ? s : 0] : qb[s % 5];
-        if (s == 0) mfma_v<DT, true>(sacc, kb[0], q);
-        else mfma_v<DT, false>(sacc, kb[s % 5], q);
+        fence();
       }
-      nops_after_mfma(sacc);
-    }
-
-    float x[16];
+    };
+    // P·V MFMAs of one tile, operands [i0, i1), V reads kVA ahead.  With
+    // WITH_DMA, this wave's 9 loads of tile dma_t (page dma_pg) go one every
+    // three MFMAs from operand 1 on.  (The P·V accumulator is in AGPRs; loads
+    // placed between the score MFMAs, whose accumulator is in VGPRs, stall
+    // far longer.)
+    auto pv_range = [&](int i0, int i1, bool with_dma, int dma_t, int dma_pg) __attribute__((always_inline)) {
+      DmaTile dt{};
+      if (i0 == 0 && with_dma) {
+        dt = cursor_tile<PAGED>(cur, dma_pg, r1, slot(dma_t));
+        cursor_next<PAGED>(cur);
+      }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = sacc[e] * p.scale_log2;
-    if (tile_base + kTileRows > r1) {   // last tile: mask rows at or past r1
+      for (int i = 0; i < 32; ++i) {
+        if (i >= i0 && i < i1) {
+          mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pk[i & 1]);
+          if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pl[i & 1]);
+          if (i + kVA < 32) vbuf[(i + kVA) % kVB] = v_read(i + kVA);
+          if (i0 == 0 && with_dma && i % 3 == 1 && i / 3 < kLoadsPerTile) issue_part(cur, dt, wave, lane16, i / 3);
+          fence();
+        }
+      }
+    };
+    // Wait for tile t+1 and for every wave to finish reading tile t-1 (whose
+    // slot tile t+3 reuses), then start the K reads of tile t+1.  Returns the
+    // page of tile t+3 (paged), loaded before the wait so that the wait
+    // covers it.  Uniform: every wave takes the same path.
+    auto advance = [&](int t) __attribute__((always_inline)) -> int {
+      int pg = 0;
+      if constexpr (PAGED) {
+        if (t + 3 < n_tiles) pg = cursor_page(cur);   // the cursor is at tile t+3
+      }
+      if (t + 2 < n_tiles) wait_cnt<kLoadsPerTile, 0>();
+      else wait_cnt<0, 0>();
+      barrier();
+      k_head(slot(t + 1));
+      fence();
+      return pg;
+    };
+
+    // ---- step 0: scores of tile 0 ------------------------------------------
+    k_head(slot(0));
+    fence();
+    phase_a(slot(0), sA, sB, false, false, slot(0));
+    int pg_next = 0;   // page of the tile whose loads the next step issues
+    if (n_tiles > 1) pg_next = advance(0);
+
+    // ---- steps 1 .. n-1, two per trip so the score tiles alternate ---------
+    // Step t issues tile t+2 into the slot of tile t-2.
+    auto step = [&](int t, f32x16& cur, f32x16& prev) __attribute__((always_inline)) {
+      phase_a(slot(t), cur, prev, true, t == 1, slot(t - 1));
+      nops_before_mfma<DT>(sm.pk, sm.pl);
+      pv_range(0, 32 - kVA, t + 2 < n_tiles, t + 2, pg_next);
+      if (t + 1 < n_tiles) pg_next = advance(t);
+      pv_range(32 - kVA, 32, false, 0, 0);
+    };
+    int t = 1;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, sB, sA);
+      step(t + 1, sA, sB);
+    }
+    if (t < n_tiles) step(t, sB, sA);
+
+    // ---- drain: softmax of tile n-1 with the tail masked, its P·V ----------
+    // Score tile k was formed in sA for even k, in sB for odd k.
+    f32x16 last = ((n_tiles - 1) & 1) ? sB : sA;
+    nops_after_mfma(last);
+    {
+      const int tile_base = r0 + (n_tiles - 1) * kTileRows;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int n = 8 * (e >> 2) + 4 * g + (e & 3);
-        if (tile_base + n >= r1) x[e] = -__builtin_inff();
+        sm.x[e] = tile_base + n < r1 ? last[e] : -__builtin_inff();
       }
+#pragma unroll
+      for (int s = 0; s < kSoftmaxSteps; ++s) sm.step(s, n_tiles == 1, c, nmc, mx, lsum);
+      v_bases(slot(n_tiles - 1));
+#pragma unroll
+      for (int i = 0; i < kVA; ++i) vbuf[i] = v_read(i);
+      nops_before_mfma<DT>(sm.pk, sm.pl);
+      fence();
+      pv_range(0, 32, false, 0, 0);
     }
-    float tmax = x[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = halves_max(tmax);
-    mx = fmaxf(mx, tmax);
-    if (!REDO) {
-      if (t == 0) m = tmax;
-      else if (__any(tmax > m + kOverflowMargin) && lane == 0) overflow = 1;
-    }
-    const float mu = (m == -__builtin_inff()) ? 0.f : m;
-
-    // -- P = 2^(x - m) as the B operand of P·V.  fp16: P rounded to fp16.
-    //    bf16: P = hi + lo, both bf16, so the product keeps ~16 bits of P.
-    float pv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(x[e] - mu);
-      lsum += pv[e];
-    }
-    u32x4 pk[2], pl[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      uint32_t w[4], wl[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = pv[8 * kt + 2 * j], cc = pv[8 * kt + 2 * j + 1];
-        w[j] = pack2<DT>(a, cc);
-        if constexpr (DT == MLA_DTYPE_BF16) {
-          const float ah = __builtin_bit_cast(float, w[j] << 16);
-          const float ch = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
-          wl[j] = pack2<DT>(a - ah, cc - ch);
-        }
-      }
-      pk[kt] = u32x4{w[0], w[1], w[2], w[3]};
-      if constexpr (DT == MLA_DTYPE_BF16) pl[kt] = u32x4{wl[0], wl[1], wl[2], wl[3]};
-    }
-
-    // -- Oᵀ[v][h] += Vᵀ[v][n] Pᵀ[n][h] over 16 blocks of 32 value columns.
-    //    Contraction slot (g, j) of k-step kt is row 16kt + 8(j/4) + 4g + (j%4),
-    //    the layout in which the score MFMA leaves P.  Operand i = 2vb + kt is
-    //    read with two transposing loads, three operands ahead.
-    {
-      // operand i = 2 vb + kt
-      auto vaddr = [&](int i, int r) -> int {
-        const int vb = i >> 1, kt = i & 1;
-        return (vofs[r] ^ (64 * (vb & 3))) + 256 * (vb >> 2) + 16384 * kt + 8192 * r;
-      };
-      u32x4 vbuf[5];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) vbuf[i] = lds_get_tr(tile, vaddr(i, 0), vaddr(i, 1));
-      nops_before_mfma<DT>(pk, pl);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + 3 < 32) vbuf[(i + 3) % 5] = lds_get_tr(tile, vaddr(i + 3, 0), vaddr(i + 3, 1));
-        mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pk[i & 1]);
-        if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % 5], pl[i & 1]);
-      }
-    }
-
+    nops_after_mfma(acc);
   }
-  nops_after_mfma(acc);
   if (!REDO) {
-    // Every wave's overflow flag write is visible after this barrier.
+    // Overflow: some tile's max passed m by more than the margin (log2
+    // units), i.e. P left the exact range of the operand type.
+    constexpr float kOverflowMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
+    const bool ovf = __any(__builtin_fmaf(mx, c, nmc) > kOverflowMargin);
+    // Agree on the flag through the first words of the tile ring, which no
+    // wave reads any more once all have passed the first barrier.
+    int* flags = reinterpret_cast<int*>(lds_raw);
     __syncthreads();
+    if (lane == 0) flags[wave] = ovf ? 1 : 0;
+    __syncthreads();
+    const bool overflow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
     if (overflow) {
       if (threadIdx.x == 0) p.redo[wi] = 1;
       if (head_ok && g == 0) p.part_lse[(int64_t)wi * p.heads + h] = mx;
@@ -499,7 +765,7 @@ void split_kernel(SplitParams p) {
   const float ltot = halves_sum(lsum);
   const bool nonempty = ltot > 0.f;
   const float inv = nonempty ? 1.f / ltot : 0.f;
-  const float lse2 = nonempty ? __log2f(ltot) + m : -__builtin_inff();
+  const float lse2 = nonempty ? __log2f(ltot) - nmc : -__builtin_inff();
   if (!head_ok) return;
   if (s_b == 1) {
     uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh;

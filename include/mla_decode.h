@@ -61,10 +61,14 @@ typedef enum mla_dtype {
 #define MLA_SPLIT_BLOCK_ROWS 64
 /* Largest number of splits of one sequence. */
 #define MLA_MAX_SPLITS 1024
+/* Cache row strides (kv_sr, kpe_sr) must be below this many elements: the
+ * kernel forms in-tile row offsets (31 rows) in 32-bit and 24-bit arithmetic. */
+#define MLA_MAX_ROW_STRIDE (1 << 22)
 
 /*
  * Problem description.  All strides are in ELEMENTS of the input dtype and must
- * keep every row start 16-byte aligned (multiples of 8 elements).
+ * keep every row start 16-byte aligned (multiples of 8 elements); kv_sr and
+ * kpe_sr must be below MLA_MAX_ROW_STRIDE (MLA_ERR_UNSUPPORTED otherwise).
  *
  * Contiguous cache (block_table == NULL):
  *   kv_latent[b, j, 0, :] at kv_latent + b*kv_sb + j*kv_sr      (512 values)
@@ -163,7 +167,8 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *   kv_latent, k_pe                         cache (see mla_desc)
  *   block_table  int32, NULL for a contiguous cache
  *   cache_seqlens int32[B], each >= 0 (a negative length gives undefined output)
- *   softmax_scale  multiplies the raw dot products (typically 1/sqrt(576))
+ *   softmax_scale  multiplies the raw dot products (typically 1/sqrt(576));
+ *                  must be finite and > 0 (MLA_ERR_INVALID_ARG otherwise)
  *   num_split  0 = planner chooses s_b per sequence; > 0 forces s_b = num_split
  *   out   [B, H, 512] dtype (strides in desc)
  *   lse   fp32 [B, H] contiguous, natural log of the sum of exp(z)

@@ -79,6 +79,9 @@ def _decode(L, desc, num_split=0, scale=1 / 24, ptrs=None, block_table=None, ws=
     ("page_16", _lib.MLA_ERR_UNSUPPORTED),
     ("page_stride0", _lib.MLA_ERR_INVALID_ARG),
     ("neg_max_seqlen", _lib.MLA_ERR_INVALID_ARG),
+    ("zero_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("neg_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("huge_row_stride", _lib.MLA_ERR_UNSUPPORTED),
 ])
 def test_validation_errors(L, case, expect):
     d = _desc()
@@ -121,6 +124,12 @@ def test_validation_errors(L, case, expect):
         kw["block_table"] = FAKE
     elif case == "neg_max_seqlen":
         d.max_seqlen = -1
+    elif case == "zero_scale":
+        kw["scale"] = 0.0
+    elif case == "neg_scale":
+        kw["scale"] = -0.04
+    elif case == "huge_row_stride":
+        d.kpe_sr = 1 << 22
     st = _decode(L, d, **kw)
     assert st == expect, (case, st, L.mla_last_error())
     assert L.mla_last_error().decode()

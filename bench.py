@@ -43,6 +43,24 @@ def workload_figures(lens, heads: int):
     return flops, kv_bytes, total_bytes
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or
+    None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        for line in open(f):
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("workload") == workload and rec.get("source_sha256") == sha:
+                    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+    return None
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the fp64 oracle on the first sequences of the workload until ~budget_s."""
     import numpy as np
@@ -184,7 +202,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": None if split_gbs is None else round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": None if split_gbs is None else round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "split_kernel"},
+                     "traffic": measured_traffic(mi.CONFIG_NAMES[args.config]), "kernel": "split_kernel"},
+        # The same launch against the dense fp16/bf16 MFMA peak (its other bound).
+        "mfma": {"achieved": None if split_avg <= 0 else round(flops / (split_avg * 1e-3) / 1e12, 1),
+                 "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": None if split_avg <= 0 else round(flops / (split_avg * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 1),
     }

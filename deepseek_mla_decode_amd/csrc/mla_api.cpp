@@ -285,20 +285,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   hipEvent_t* ev = timing_slot();
   if (ev) (void)hipEventRecord(ev[0], stream);
 
-  if (num_split == 0) {
-    mla::PlanParams pp{};
-    pp.seqlens = cache_seqlens;
-    pp.num_splits = num_splits;
-    pp.split_offset = split_offset;
-    pp.work = work;
-    pp.batch = d->batch;
-    pp.heads = d->heads;
-    pp.num_split = 0;
-    pp.num_cus = num_cus;
-    pp.row_cap = row_cap;
-    if ((e = mla::launch_plan(pp, stream)) != hipSuccess)
-      return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
-  }
+  // In planner mode the split kernel plans for itself (no planner launch).
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   mla::SplitParams sp{};
@@ -308,13 +295,14 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.kpe = static_cast<const uint16_t*>(k_pe);
   sp.block_table = block_table;
   sp.seqlens = cache_seqlens;
-  sp.work = work;
+  sp.num_splits = num_splits;
   sp.split_offset = split_offset;
+  sp.work = work;
+  sp.redo = redo;
   sp.out = static_cast<uint16_t*>(out);
   sp.lse = lse;
   sp.part_o = part_o;
   sp.part_lse = part_lse;
-  sp.redo = redo;
   sp.q_nope_sb = d->q_nope_sb;
   sp.q_nope_sh = d->q_nope_sh;
   sp.q_pe_sb = d->q_pe_sb;
@@ -332,6 +320,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.bt_stride = paged ? d->block_table_stride : 0;
   sp.num_pages = paged ? d->num_pages : 0;
   sp.row_cap = row_cap;
+  sp.num_cus = num_cus;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;
   if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream)) !=
       hipSuccess)

@@ -15,13 +15,14 @@ struct SplitParams {
   const uint16_t* kpe;          // RoPE part of cache rows
   const int32_t* block_table;   // paged only
   const int32_t* seqlens;
-  const int32_t* work;          // planner mode: work list (4 ints per item)
-  const int32_t* split_offset;  // planner mode: [B + 1]
+  int32_t* num_splits;          // planner mode: written by workgroup 0 for the combine
+  int32_t* split_offset;        // planner mode: [B + 1], written by workgroup 0
+  int32_t* work;                // planner mode: work list (4 ints per item), written by workgroup 0
+  int32_t* redo;                // [max_work]: main pass overflowed, rerun with the exact max
   uint16_t* out;
   float* lse;
   float* part_o;                // [max_work, H, 512]
   float* part_lse;              // [max_work, H], base 2
-  int32_t* redo;                // [max_work]: main pass overflowed, rerun with the exact max
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
   int64_t out_sb, out_sh;
@@ -30,6 +31,7 @@ struct SplitParams {
   int32_t page_size, bt_stride;
   int32_t num_pages;            // paged: page indices are clamped to [0, num_pages)
   int32_t row_cap;              // lengths are clamped to [0, row_cap]
+  int32_t num_cus;              // planner mode: the planner's CU count
   float scale_log2;             // softmax_scale * log2(e)
 };
 

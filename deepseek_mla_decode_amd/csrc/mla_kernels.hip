@@ -125,6 +125,9 @@ __device__ __forceinline__ void nops_before_mfma(u32x4 (&x)[2], u32x4 (&y)[2]) {
 // the same in both halves.  Written as asm with two distinct registers: the
 // builtin, given the same value twice, is folded as if both results were equal.
 // The leading s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
 __device__ __forceinline__ void swap_halves(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
@@ -223,6 +226,181 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 }
 
 // ---------------------------------------------------------------------------
+// Split planner inside the split kernel
+// ---------------------------------------------------------------------------
+// In planner mode every wave of the main pass runs the planner rule of
+// plan_rule.h itself, on one wave with no barrier: the same integers as the
+// host twin and the stand-alone planner kernel.  This saves a kernel launch
+// per call.  Workgroup 0 publishes the plan (num_splits, split_offset, work)
+// for the rerun launch and the combine kernel.
+
+// Sum and max over the 64 lanes: DPP within each row of 16 lanes (pairs,
+// quads, halves, rows), then the four row results through readlane.  Every
+// lane must be active.
+__device__ __forceinline__ int row_sum_i32(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v = row_sum_i32(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Exclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  return inc - v;
+}
+
+struct WorkItem {
+  int b, k, r0, r1, s_b;
+  bool valid;   // false: past the last work item of the plan
+};
+
+// Sequences per lane whose lengths the planner keeps in registers (batch <=
+// 256); larger batches re-read the lengths where they need them.
+constexpr int kPlanRegs = 4;
+
+__device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publish) {
+  const int B = p.batch;
+  // Lane l owns the contiguous sequences [b0, b1); per is uniform.
+  const int per = (B + 63) / 64;
+  const int b0 = min(B, lane * per), b1 = min(B, b0 + per);
+  const bool in_regs = per <= kPlanRegs;
+  int Lr[kPlanRegs];   // clamped lengths of the lane's sequences
+#pragma unroll
+  for (int j = 0; j < kPlanRegs; ++j) {
+    Lr[j] = -1;
+    if (in_regs && j < per && b0 + j < b1) Lr[j] = clamp_len(p.seqlens[b0 + j], p.row_cap);
+  }
+  // Length of the lane's j-th sequence b = b0 + j (-1 past its last).
+  auto len_of = [&](int j, int b) __attribute__((always_inline)) -> int {
+    if (in_regs) {
+      int L = -1;
+#pragma unroll
+      for (int jj = 0; jj < kPlanRegs; ++jj)
+        if (jj == j) L = Lr[jj];
+      return L;
+    }
+    return clamp_len(p.seqlens[b], p.row_cap);
+  };
+  // Splits of the lane's sequences under budget t.
+  auto lane_splits = [&](int t) __attribute__((always_inline)) -> int {
+    int cnt = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kPlanRegs; ++j)
+        if (j < per) cnt += Lr[j] >= 0 ? splits_for_budget(num_blocks(Lr[j]), t) : 0;
+    } else {
+      for (int b = b0; b < b1; ++b) cnt += splits_for_budget(num_blocks(clamp_len(p.seqlens[b], p.row_cap)), t);
+    }
+    return cnt;
+  };
+  int maxnb = 0;
+  int64_t sumnb = 0;
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j)
+      if (j < per) {
+        const int nb = Lr[j] >= 0 ? num_blocks(Lr[j]) : 0;
+        maxnb = max(maxnb, nb);
+        sumnb += nb;
+      }
+  } else {
+    for (int b = b0; b < b1; ++b) {
+      const int nb = num_blocks(clamp_len(p.seqlens[b], p.row_cap));
+      maxnb = max(maxnb, nb);
+      sumnb += nb;
+    }
+  }
+  maxnb = wave_max_i32(maxnb);
+  sumnb = wave_sum_i64(sumnb);
+  // Smallest budget t with sum_b splits_for_budget(nb_b, t) <= cap; the sum
+  // is at least sum_b nb_b / t, so t starts at ceil(sum nb / cap).
+  const int cap = planner_cap(B, p.heads, p.num_cus);
+  int hi = maxnb > 1 ? maxnb : 1;
+  int64_t lo64 = (sumnb + cap - 1) / cap;
+  int lo = (int)(lo64 < 1 ? 1 : (lo64 > hi ? hi : lo64));
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (wave_sum_i32(lane_splits(mid)) <= cap) hi = mid;
+    else lo = mid + 1;
+  }
+  const int t = lo;
+  const int mine = lane_splits(t);
+  const int off = wave_excl_scan(mine, lane);
+  const int total = __shfl(off + mine, 63);
+  if (publish) {
+    int o = off;
+    for (int b = b0; b < b1; ++b) {
+      const int L = clamp_len(p.seqlens[b], p.row_cap);
+      const int sb = splits_for_budget(num_blocks(L), t);
+      p.num_splits[b] = sb;
+      p.split_offset[b] = o;
+      for (int k = 0; k < sb; ++k) {
+        int r0, r1;
+        split_range(L, sb, k, &r0, &r1);
+        int* w = p.work + 4 * (o + k);
+        w[0] = b;
+        w[1] = k;
+        w[2] = r0;
+        w[3] = r1;
+      }
+      o += sb;
+    }
+    if (lane == 63) p.split_offset[B] = total;
+  }
+  WorkItem it{};
+  it.valid = wi < total;
+  if (!it.valid) return it;
+  // The lane whose chunk holds work item wi finds its sequence and split.
+  const uint64_t owner_mask = __ballot(wi >= off && wi < off + mine);
+  const int owner = __builtin_ctzll(owner_mask);
+  int fb = 0, fk = 0, fL = 0;
+  if (lane == owner) {
+    int o = off;
+    for (int b = b0; b < b1; ++b) {
+      const int L = len_of(b - b0, b);
+      const int sb = splits_for_budget(num_blocks(L), t);
+      if (wi < o + sb) {
+        fb = b;
+        fk = wi - o;
+        fL = L;
+        break;
+      }
+      o += sb;
+    }
+  }
+  it.b = __shfl(fb, owner);
+  it.k = __shfl(fk, owner);
+  const int L = __shfl(fL, owner);
+  it.s_b = splits_for_budget(num_blocks(L), t);
+  split_range(L, it.s_b, it.k, &it.r0, &it.r1);
+  return it;
+}
+
+// ---------------------------------------------------------------------------
 // Split kernel
 // ---------------------------------------------------------------------------
 
@@ -274,6 +452,15 @@ __device__ __forceinline__ void dma16_rope(const void* base, int w8, int nlast, 
 __device__ __forceinline__ uint32_t xor_add(uint32_t sbase, uint32_t key, uint32_t lane_bits) {
   uint32_t r;
   asm volatile("v_xor_b32 %0, %1, %2\n\tv_add_u32 %0, %3, %0" : "=&v"(r) : "s"(key), "v"(lane_bits), "s"(sbase));
+  return r;
+}
+
+// a ^ K as an opaque VALU op, formed where it is used: the compiler would
+// otherwise keep it in a register through the tile loop.
+template <uint32_t K>
+__device__ __forceinline__ uint32_t xor_imm(uint32_t a) {
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(K), "v"(a));
   return r;
 }
 
@@ -470,7 +657,15 @@ void split_kernel(SplitParams p) {
     const int k = wi - b * p.num_split;
     split_range(clamp_len(p.seqlens[b], p.row_cap), p.num_split, k, &r0, &r1);
     s_b = p.num_split;
+  } else if (!REDO) {
+    const WorkItem it = plan_item(p, wi, lane, wi == 0 && blockIdx.y == 0 && wave == 0);
+    if (!it.valid) return;
+    b = it.b;
+    r0 = it.r0;
+    r1 = it.r1;
+    s_b = it.s_b;
   } else {
+    // The plan the main pass published.
     if (wi >= p.split_offset[p.batch]) return;
     b = p.work[4 * wi + 0];
     r0 = p.work[4 * wi + 2];
@@ -593,7 +788,7 @@ void split_kernel(SplitParams p) {
     constexpr int kVA = DT == MLA_DTYPE_F16 ? 3 : 2;
     constexpr int kKB = kKA + 1, kVB = kVA + 1;
     u32x4 kb[kKB], vbuf[kVB], qb[4];
-    uint32_t kq[8], vw[2][4];
+    uint32_t kq[8], vw[4];
     f32x16 sA, sB;
     Softmax<DT, REDO> sm;
 
@@ -617,23 +812,17 @@ void split_kernel(SplitParams p) {
     auto v_bases = [&](const lds_char* tile) __attribute__((always_inline)) {
       const uint32_t base = lds_u32(tile);
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) vw[r][cc] = xor_add(base, 64u * cc + 32u * r, vofs0);
+      for (int cc = 0; cc < 4; ++cc) vw[cc] = xor_add(base, 64u * cc, vofs0);
     };
     auto v_read = [&](int i) __attribute__((always_inline)) -> u32x4 {
       const int vb = i >> 1, kt = i & 1;
       const int imm = 256 * (vb >> 2) + 16384 * kt;
-      return lds_get_tr(lds_at(vw[0][vb & 3]), imm, lds_at(vw[1][vb & 3]), imm + 8192);
+      // Half r = 1 is half 0 with bit 5 flipped (the tile base is 1 KiB aligned).
+      return lds_get_tr(lds_at(vw[vb & 3]), imm, lds_at(xor_imm<32>(vw[vb & 3])), imm + 8192);
     };
     // Score MFMAs of one tile into `sc`; with WITH_SM, the softmax of the
     // previous tile runs between them and the first kVA V reads of the
     // previous tile are issued at the end.
-    // With WITH_DMA, this wave's loads of tile dma_t (page dma_pg) are issued
-    // one every four MFMAs, wave w in the slots s = w (mod 4): the CU's
-    // vector-memory path takes a 1 KiB load every dozen or so cycles, and
-    // loads issued together (by one wave, or by the four waves at once) stall
-    // the issuing wave, and with it its MFMAs.
     auto phase_a = [&](const lds_char* tile, f32x16& sc, f32x16& prev, bool with_sm, bool first_prev,
                        const lds_char* vtile) __attribute__((always_inline)) {
       if (with_sm) {
@@ -659,9 +848,12 @@ void split_kernel(SplitParams p) {
     };
     // P·V MFMAs of one tile, operands [i0, i1), V reads kVA ahead.  With
     // WITH_DMA, this wave's 9 loads of tile dma_t (page dma_pg) go one every
-    // three MFMAs from operand 1 on.  (The P·V accumulator is in AGPRs; loads
-    // placed between the score MFMAs, whose accumulator is in VGPRs, stall
-    // far longer.)
+    // three MFMAs: the CU's vector-memory path takes a 1 KiB load only every
+    // dozen or so cycles, and a wave stalls at issue until its load is taken
+    // (about 20 cycles alone, about 50 when all four waves issue together),
+    // so loads issued in a burst stall the MFMAs behind them.  (Loads placed
+    // between the score MFMAs, whose accumulator is in VGPRs, stalled longer
+    // still.)
     auto pv_range = [&](int i0, int i1, bool with_dma, int dma_t, int dma_pg) __attribute__((always_inline)) {
       DmaTile dt{};
       if (i0 == 0 && with_dma) {
@@ -672,9 +864,10 @@ void split_kernel(SplitParams p) {
       for (int i = 0; i < 32; ++i) {
         if (i >= i0 && i < i1) {
           mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pk[i & 1]);
+          // A load right behind an MFMA, its issue stall overlapping the MFMA.
+          if (i0 == 0 && with_dma && i % 3 == 1 && i / 3 < kLoadsPerTile) issue_part(cur, dt, wave, lane16, i / 3);
           if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pl[i & 1]);
           if (i + kVA < 32) vbuf[(i + kVA) % kVB] = v_read(i + kVA);
-          if (i0 == 0 && with_dma && i % 3 == 1 && i / 3 < kLoadsPerTile) issue_part(cur, dt, wave, lane16, i / 3);
           fence();
         }
       }
@@ -727,7 +920,7 @@ void split_kernel(SplitParams p) {
       const int tile_base = r0 + (n_tiles - 1) * kTileRows;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int n = 8 * (e >> 2) + 4 * g + (e & 3);
+        const int n = 8 * (e >> 2) + 4 * (lane_id() >> 5) + (e & 3);
         sm.x[e] = tile_base + n < r1 ? last[e] : -__builtin_inff();
       }
 #pragma unroll
@@ -741,6 +934,12 @@ void split_kernel(SplitParams p) {
     }
     nops_after_mfma(acc);
   }
+  // Lane, head and half again, from the lane id rather than the workitem id,
+  // so that none of them stays live through the tile loop.
+  const int lane_t = lane_id();
+  const int g_t = lane_t >> 5;
+  const int h_t = h0 + (lane_t & 31);
+  const bool head_ok_t = h_t < p.heads;
   if (!REDO) {
     // Overflow: some tile's max passed m by more than the margin (log2
     // units), i.e. P left the exact range of the operand type.
@@ -750,15 +949,15 @@ void split_kernel(SplitParams p) {
     // wave reads any more once all have passed the first barrier.
     int* flags = reinterpret_cast<int*>(lds_raw);
     __syncthreads();
-    if (lane == 0) flags[wave] = ovf ? 1 : 0;
+    if (lane_t == 0) flags[wave] = ovf ? 1 : 0;
     __syncthreads();
     const bool overflow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
     if (overflow) {
-      if (threadIdx.x == 0) p.redo[wi] = 1;
-      if (head_ok && g == 0) p.part_lse[(int64_t)wi * p.heads + h] = mx;
+      if (wave == 0 && lane_t == 0) p.redo[wi] = 1;
+      if (head_ok_t && g_t == 0) p.part_lse[(int64_t)wi * p.heads + h_t] = mx;
       return;
     }
-    if (threadIdx.x == 0) p.redo[wi] = 0;
+    if (wave == 0 && lane_t == 0) p.redo[wi] = 0;
   }
 
   // ---- epilogue: normalise; write final output or the split partial --------
@@ -766,34 +965,34 @@ void split_kernel(SplitParams p) {
   const bool nonempty = ltot > 0.f;
   const float inv = nonempty ? 1.f / ltot : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) - nmc : -__builtin_inff();
-  if (!head_ok) return;
+  if (!head_ok_t) return;
   if (s_b == 1) {
-    uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh;
+    uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h_t * p.out_sh;
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int v = 32 * vb + 8 * q + 4 * g;
+        const int v = 32 * vb + 8 * q + 4 * g_t;
         u32x2 w;
         w.x = pack2<DT>(acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv);
         w.y = pack2<DT>(acc[vb][4 * q + 2] * inv, acc[vb][4 * q + 3] * inv);
         *reinterpret_cast<u32x2*>(o + v) = w;
       }
     }
-    if (g == 0) p.lse[(int64_t)b * p.heads + h] = nonempty ? lse2 * kLn2 : -__builtin_inff();
+    if (g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
   } else {
-    float* o = p.part_o + ((int64_t)wi * p.heads + h) * 512;
+    float* o = p.part_o + ((int64_t)wi * p.heads + h_t) * 512;
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int v = 32 * vb + 8 * q + 4 * g;
+        const int v = 32 * vb + 8 * q + 4 * g_t;
         f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
                    acc[vb][4 * q + 3] * inv};
         *reinterpret_cast<f32x4*>(o + v) = w;
       }
     }
-    if (g == 0) p.part_lse[(int64_t)wi * p.heads + h] = lse2;
+    if (g_t == 0) p.part_lse[(int64_t)wi * p.heads + h_t] = lse2;
   }
 }
 

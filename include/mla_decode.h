@@ -135,8 +135,8 @@ int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32
 
 /*
  * Bytes of device workspace mla_decode needs for this description:
- *   plan (int32): B + (B+1) + 4*max_work, then max_work redo flags, rounded
- *   to 256 bytes; partial lse (fp32, base 2): max_work * H, rounded to 256;
+ *   plan (int32): B + (B+1) + 4*max_work, then max_work rerun flags,
+ *   rounded to 256 bytes; partial lse (fp32, base 2): max_work * H, rounded to 256;
  *   partial out (fp32): max_work * H * 512, rounded to 256.
  */
 int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
@@ -175,11 +175,12 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *   workspace  device buffer of at least mla_workspace_size() bytes, 256-byte
  *              aligned; its contents on entry do not matter.
  * A sequence with L_b = 0 gets out = 0 and lse = -inf.
- * Launches: planner (planner mode only), split kernel, a second split launch
- * that only reruns work items whose scores spread beyond the range of P for
- * the reference max taken from their first tile (all other workgroups exit at
- * once), and the combine kernel (only touches sequences with s_b > 1; a single
- * split writes out/lse directly).
+ * Launches: the split kernel (in planner mode each of its workgroups runs the
+ * planner rule itself and workgroup 0 writes the plan into the workspace); a
+ * second split launch that only reruns work items whose scores spread beyond
+ * the range of P for the reference max taken from their first tile (all other
+ * workgroups exit at once); the combine kernel (only touches sequences with
+ * s_b > 1; a single split writes out/lse directly).
  * Calls that share a workspace must be ordered on one stream.
  */
 int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
@@ -192,7 +193,9 @@ const char* mla_last_error(void);
 
 /*
  * Kernel timing for measurement.  While enabled, every mla_decode call records
- * HIP events around its planner, split and combine launches on its stream.
+ * HIP events around its launches on its stream: plan_ms brackets no launch
+ * (the split kernel plans for itself) and reads ~0, split_ms covers both split
+ * launches, combine_ms the combine.
  * mla_timing_read() synchronises on those events and returns the summed
  * milliseconds and the number of calls since the last read (then resets).
  * Up to 4096 calls are recorded between reads; later ones are not timed.

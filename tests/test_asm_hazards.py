@@ -48,15 +48,23 @@ def test_checker_flags_a_planted_early_read(asm):
 
 
 def _loop_bodies(asm, kernel):
+    """Lines of each innermost loop of `kernel`: its header block and every
+    block the compiler's comments place in it (wherever the layout puts them)."""
     lines = asm.split("\n")
     start = next(i for i, l in enumerate(lines) if l.startswith(kernel + ":"))
     end = next((i for i in range(start + 1, len(lines)) if re.match(r"^_Z\w+:", lines[i])), len(lines))
     body = lines[start:end]
-    for h, x in enumerate(body):
-        if "Inner Loop Header" in x:
-            label = x.split(":")[0].replace(".LBB", "BB")
-            last = max(i for i, y in enumerate(body) if "Header=" + label in y)
-            yield body[h:last + 1]
+    blocks = []   # (label, comment text, lines)
+    for i, x in enumerate(body):
+        if re.match(r"^\.LBB\w+:", x):
+            comment = x + (body[i + 1] if i + 1 < len(body) and body[i + 1].lstrip().startswith(";") else "")
+            blocks.append((x.split(":")[0], comment, [x]))
+        elif blocks:
+            blocks[-1][2].append(x)
+    for label, comment, blines in blocks:
+        if "Inner Loop Header" in comment:
+            tag = "Header=" + label.replace(".LBB", "BB")
+            yield blines + [y for lab, com, bl in blocks if tag in com.split(";", 1)[-1] and lab != label for y in bl]
 
 
 def test_tile_loops_do_not_touch_scratch(asm):

@@ -242,3 +242,36 @@ def test_late_dominant_key_reruns_with_exact_max(mla, dtype, boost):
         out, lse = _run(mla, inp, ns)
         ro, rl = oracle.mla_decode_ref(inp)
         assert_parity(out, lse, ro, rl, f"dominant key {dtype} boost={boost} split={ns}")
+
+
+@pytest.mark.parametrize("B", [5, 64, 200, 300, 1000])
+def test_split_kernel_publishes_the_host_plan(mla, B):
+    """In planner mode the split kernel plans for itself; workgroup 0 writes
+    the plan into the workspace.  It must equal the host twin's integers, for
+    batches whose block counts sit in registers (<= 256 sequences) and for
+    larger ones, and the output must still match the oracle."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    rng = np.random.default_rng(200 + B)
+    lens = rng.integers(0, 300, size=B).astype(np.int32)
+    lens[rng.integers(0, B)] = 0
+    inp = mi.make_contiguous(B, 128, 300, lens, "f16", seed=110)
+    d = to_device(inp, "cuda")
+    cus = mla.mla_num_cus(0)
+    hn, ho, hw = mla.mla_plan_host(lens, 128, 0, cus)
+    out = torch.empty((B, 128, 512), dtype=torch.float16, device="cuda")
+    desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, out)
+    ws = torch.empty(mla.mla_workspace_size(desc, 0, cus), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)
+    out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"],
+                              inp.softmax_scale, num_split=0, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    # Workspace layout: num_splits [B], split_offset [B + 1], work [W][4].
+    plan = ws[: 4 * (B + B + 1 + 4 * int(ho[-1]))].view(torch.int32).cpu().numpy()
+    assert np.array_equal(plan[:B], hn)
+    assert np.array_equal(plan[B:2 * B + 1], ho)
+    assert np.array_equal(plan[2 * B + 1:].reshape(-1, 4), hw.reshape(-1, 4)[: int(ho[-1])])
+    samples = sorted({0, B // 2, B - 1, int(np.argmax(lens))})
+    for b in samples:
+        ro, rl = oracle.mla_decode_ref(inp, batches=[b])
+        assert_parity(from_device(out)[b:b + 1], from_device(lse)[b:b + 1], ro, rl, f"B={B} seq {b}")

@@ -146,8 +146,9 @@ __device__ __forceinline__ float halves_sum(float x) {
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   if constexpr (DT == MLA_DTYPE_F16) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));   // one v_cvt_pk_f16_f32
   } else {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
@@ -515,19 +516,23 @@ __device__ __forceinline__ DmaTile cursor_tile(const DmaCursor& c, int page, int
   return d;
 }
 
+// Next tile, except that the cursor stays on the work item's last tile (the
+// one holding row r1 - 1): the loop loads a tile every step, and past the end
+// it reloads that last tile (valid memory) into a slot nothing reads again.
+// Branch-free (a branch here splits the loop body and costs register copies
+// at the join).
 template <bool PAGED>
-__device__ __forceinline__ void cursor_next(DmaCursor& c) {
-  c.row += kTileRows;
+__device__ __forceinline__ void cursor_next(DmaCursor& c, int r1) {
+  const int adv = c.row + kTileRows < r1 ? 1 : 0;
+  c.row += adv * kTileRows;
   if constexpr (PAGED) {
-    // Branch-free (a branch here splits the loop body and costs register
-    // copies at the join).
-    c.in_page += kTileRows;
+    c.in_page += adv * kTileRows;
     const int wrap = c.in_page == c.page_size ? 1 : 0;
     c.in_page -= wrap * c.page_size;
     c.bt += wrap;
   } else {
-    c.lat += (int64_t)kTileRows * c.lat_rb;
-    c.rope += (int64_t)kTileRows * c.rope_rb;
+    c.lat += (int64_t)(adv * kTileRows) * c.lat_rb;
+    c.rope += (int64_t)(adv * kTileRows) * c.rope_rb;
   }
 }
 
@@ -764,19 +769,17 @@ void split_kernel(SplitParams p) {
   {
     // ---- prologue ----------------------------------------------------------
     {
+      // Always three tiles (the last one again past the end), so that every
+      // wait below counts the same loads.
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        if (k < n_tiles) {
-          const int pg = PAGED ? cursor_page(cur) : 0;
-          const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(k));
+        const int pg = PAGED ? cursor_page(cur) : 0;
+        const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(k));
 #pragma unroll
-          for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
-          cursor_next<PAGED>(cur);
-        }
+        for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+        cursor_next<PAGED>(cur, r1);
       }
-      if (n_tiles > 2) wait_cnt<2 * kLoadsPerTile, 15>();
-      else if (n_tiles > 1) wait_cnt<kLoadsPerTile, 15>();
-      else wait_cnt<0, 15>();
+      wait_cnt<2 * kLoadsPerTile, 15>();
       barrier();
     }
 
@@ -858,7 +861,7 @@ void split_kernel(SplitParams p) {
       DmaTile dt{};
       if (i0 == 0 && with_dma) {
         dt = cursor_tile<PAGED>(cur, dma_pg, r1, slot(dma_t));
-        cursor_next<PAGED>(cur);
+        cursor_next<PAGED>(cur, r1);
       }
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
@@ -878,11 +881,8 @@ void split_kernel(SplitParams p) {
     // covers it.  Uniform: every wave takes the same path.
     auto advance = [&](int t) __attribute__((always_inline)) -> int {
       int pg = 0;
-      if constexpr (PAGED) {
-        if (t + 3 < n_tiles) pg = cursor_page(cur);   // the cursor is at tile t+3
-      }
-      if (t + 2 < n_tiles) wait_cnt<kLoadsPerTile, 0>();
-      else wait_cnt<0, 0>();
+      if constexpr (PAGED) pg = cursor_page(cur);   // the cursor is at tile t+3 (or the last)
+      wait_cnt<kLoadsPerTile, 0>();
       barrier();
       k_head(slot(t + 1));
       fence();
@@ -898,11 +898,13 @@ void split_kernel(SplitParams p) {
 
     // ---- steps 1 .. n-1, two per trip so the score tiles alternate ---------
     // Step t issues tile t+2 into the slot of tile t-2.
+    // Every step loads a tile and passes a barrier, also the last ones (see
+    // cursor_next), so that the loop has no branch but its back edge.
     auto step = [&](int t, f32x16& cur, f32x16& prev) __attribute__((always_inline)) {
       phase_a(slot(t), cur, prev, true, t == 1, slot(t - 1));
       nops_before_mfma<DT>(sm.pk, sm.pl);
-      pv_range(0, 32 - kVA, t + 2 < n_tiles, t + 2, pg_next);
-      if (t + 1 < n_tiles) pg_next = advance(t);
+      pv_range(0, 32 - kVA, true, t + 2, pg_next);
+      pg_next = advance(t);
       pv_range(32 - kVA, 32, false, 0, 0);
     };
     int t = 1;
@@ -932,6 +934,9 @@ void split_kernel(SplitParams p) {
       fence();
       pv_range(0, 32, false, 0, 0);
     }
+    // No load may still be writing the ring when the ending reuses it or the
+    // workgroup leaves.
+    wait_cnt<0, 15>();
     nops_after_mfma(acc);
   }
   // Lane, head and half again, from the lane id rather than the workitem id,

@@ -343,7 +343,9 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     cp.out_sh = d->out_sh;
     cp.num_split = num_split;
     cp.heads = d->heads;
-    if ((e = mla::launch_combine(cp, d->dtype, d->batch, stream)) != hipSuccess)
+    // Splits per sequence on average: forced, or at most max_work / B.
+    const int mean_splits = num_split > 0 ? num_split : (max_work + d->batch - 1) / (d->batch > 0 ? d->batch : 1);
+    if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream)) != hipSuccess)
       return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   }
   if (ev) (void)hipEventRecord(ev[3], stream);

@@ -58,6 +58,9 @@ struct PlanParams {
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
                         hipStream_t stream);
-hipError_t launch_combine(const CombineParams& p, int dtype, int batch, hipStream_t stream);
+// mean_splits: splits per sequence, on average (forced count, or the plan's
+// bound over the batch); from kCombineSplitkMin on, four waves share a head.
+constexpr int kCombineSplitkMin = 16;
+hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream);
 
 }  // namespace mla

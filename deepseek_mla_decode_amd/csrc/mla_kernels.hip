@@ -1002,7 +1002,11 @@ void split_kernel(SplitParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: grid (ceil(H / 4), B), one wave per head, 8 values per lane.
+// Combine kernels.  combine_heads_kernel: grid (ceil(H / 4), B), one wave per
+// head, 8 output values per lane; for sequences of few splits.
+// combine_splitk_kernel: grid (H, B), four waves per head; for many splits,
+// where one wave per head would leave most of the GPU idle.  Both form the
+// final LSE from all split lse values first, then the weighted sum.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -1016,13 +1020,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int b = blockIdx.y;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (h >= p.heads) return;
-  int s, base;
+constexpr int kCombineUnroll = 8;   // splits per wave whose reads are in flight together
+
+// Number of splits of sequence b and its first work item.
+__device__ __forceinline__ void combine_range(const CombineParams& p, int b, int& s, int& base) {
   if (p.num_split > 0) {
     s = p.num_split;
     base = b * p.num_split;
@@ -1030,6 +1031,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     base = p.split_offset[b];
     s = p.split_offset[b + 1] - base;
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= p.heads) return;
+  int s, base;
+  combine_range(p, b, s, base);
   if (s <= 1) return;
 
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
@@ -1063,6 +1074,81 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   r.w = pack2<DT>(a1.z, a1.w);
   *reinterpret_cast<u32x4*>(o) = r;
   if (lane == 0) p.lse[(int64_t)b * p.heads + h] = total * kLn2;
+}
+
+// Wave w accumulates splits w, w + 4, ... (8 output values per lane, eight
+// splits' reads in flight); the four sums meet in LDS, and wave w writes
+// output columns 128 w .. 128 w + 127.
+template <int DT>
+__global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
+  __shared__ f32x4 red[4][2][64];   // [wave][half][lane]: 8 values per lane
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int s, base;
+  combine_range(p, b, s, base);
+  if (s <= 1) return;   // uniform: one split wrote out/lse itself
+
+  const float* L = p.part_lse + (int64_t)base * p.heads + h;
+  float mx = -__builtin_inff();
+  for (int k = lane; k < s; k += 64) mx = fmaxf(mx, L[(int64_t)k * p.heads]);
+  mx = wave_max(mx);
+  if (mx == -__builtin_inff()) {   // every split empty
+    if (wave == 0) {
+      uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 8 * lane;
+      *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
+      if (lane == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
+    }
+    return;
+  }
+  float se = 0.f;
+  for (int k = lane; k < s; k += 64) se += __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - mx);
+  se = wave_sum(se);
+  const float total = __log2f(se) + mx;
+
+  // This wave's splits: k = wave + 4 i.
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  const int64_t stride = (int64_t)p.heads * 512;   // floats between consecutive splits
+  const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
+  int k = wave;
+  for (; k + 4 * (kCombineUnroll - 1) < s; k += 4 * kCombineUnroll) {
+    f32x4 v0[kCombineUnroll], v1[kCombineUnroll];
+    float w[kCombineUnroll];
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)(k + 4 * u) * stride);
+      v0[u] = src[0];
+      v1[u] = src[1];
+      w[u] = L[(int64_t)(k + 4 * u) * p.heads];
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const float wu = __builtin_amdgcn_exp2f(w[u] - total);
+      a0 += wu * v0[u];
+      a1 += wu * v1[u];
+    }
+  }
+  for (; k < s; k += 4) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
+    const float wu = __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - total);
+    a0 += wu * src[0];
+    a1 += wu * src[1];
+  }
+  red[wave][0][lane] = a0;
+  red[wave][1][lane] = a1;
+  __syncthreads();
+  // Wave w: columns 128 w + 2 lane, + 1 (lane pair 16 w + lane / 4 of the
+  // 8-value lanes above, half (lane / 2) % 2, element pair lane % 2).
+  const int src_lane = 16 * wave + (lane >> 2), half = (lane >> 1) & 1, e = 2 * (lane & 1);
+  float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const f32x4 q = red[v][half][src_lane];
+    c0 += q[e];
+    c1 += q[e + 1];
+  }
+  uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 128 * wave + 2 * lane;
+  *reinterpret_cast<uint32_t*>(o) = pack2<DT>(c0, c1);
+  if (wave == 0 && lane == 0) p.lse[(int64_t)b * p.heads + h] = total * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1185,10 +1271,17 @@ hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x,
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineParams& p, int dtype, int batch, hipStream_t stream) {
-  const dim3 grid((p.heads + 3) / 4, batch), block(256);
-  if (dtype == MLA_DTYPE_F16) hipLaunchKernelGGL(combine_kernel<MLA_DTYPE_F16>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(combine_kernel<MLA_DTYPE_BF16>, grid, block, 0, stream, p);
+hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream) {
+  const dim3 block(256);
+  if (mean_splits >= kCombineSplitkMin) {
+    const dim3 grid(p.heads, batch);
+    if (dtype == MLA_DTYPE_F16) hipLaunchKernelGGL(combine_splitk_kernel<MLA_DTYPE_F16>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(combine_splitk_kernel<MLA_DTYPE_BF16>, grid, block, 0, stream, p);
+  } else {
+    const dim3 grid((p.heads + 3) / 4, batch);
+    if (dtype == MLA_DTYPE_F16) hipLaunchKernelGGL(combine_heads_kernel<MLA_DTYPE_F16>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(combine_heads_kernel<MLA_DTYPE_BF16>, grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

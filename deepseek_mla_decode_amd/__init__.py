@@ -213,7 +213,7 @@ def mla_timing_enable(enable: bool = True) -> None:
 
 
 def mla_timing_read():
-    """(plan_ms, split_ms, combine_ms, calls) summed since the last read."""
+    """(split_ms, rerun_ms, combine_ms, calls) summed since the last read."""
     a, b, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
     n = ctypes.c_int32()
     _lib.check(_lib.lib().mla_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(n)))

@@ -282,12 +282,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   float* part_o = reinterpret_cast<float*>(ws + L.part_o);
 
-  hipEvent_t* ev = timing_slot();
-  if (ev) (void)hipEventRecord(ev[0], stream);
-
   // In planner mode the split kernel plans for itself (no planner launch).
-  if (ev) (void)hipEventRecord(ev[1], stream);
-
   mla::SplitParams sp{};
   sp.q_nope = static_cast<const uint16_t*>(q_nope);
   sp.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -322,9 +317,12 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.row_cap = row_cap;
   sp.num_cus = num_cus;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipEvent_t* ev = timing_slot();
+  if (ev) (void)hipEventRecord(ev[0], stream);
   if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream)) !=
       hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
+  if (ev) (void)hipEventRecord(ev[1], stream);
   // Work items whose main pass overflowed the P range are redone with their
   // exact max; every other workgroup of this launch exits at once.
   if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), true, stream)) !=
@@ -359,8 +357,8 @@ int mla_timing_enable(int enable) {
   return ok();
 }
 
-int mla_timing_read(float* plan_ms, float* split_ms, float* combine_ms, int32_t* calls) {
-  if (!plan_ms || !split_ms || !combine_ms || !calls) return fail(MLA_ERR_INVALID_ARG, "NULL output");
+int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t* calls) {
+  if (!split_ms || !rerun_ms || !combine_ms || !calls) return fail(MLA_ERR_INVALID_ARG, "NULL output");
   std::lock_guard<std::mutex> lk(g_tmu);
   double acc[3] = {0, 0, 0};
   for (int i = 0; i < g_timed; ++i) {
@@ -374,8 +372,8 @@ int mla_timing_read(float* plan_ms, float* split_ms, float* combine_ms, int32_t*
       acc[k] += ms;
     }
   }
-  *plan_ms = (float)acc[0];
-  *split_ms = (float)acc[1];
+  *split_ms = (float)acc[0];
+  *rerun_ms = (float)acc[1];
   *combine_ms = (float)acc[2];
   *calls = g_timed;
   g_timed = 0;

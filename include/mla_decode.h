@@ -193,15 +193,15 @@ const char* mla_last_error(void);
 
 /*
  * Kernel timing for measurement.  While enabled, every mla_decode call records
- * HIP events around its launches on its stream: plan_ms brackets no launch
- * (the split kernel plans for itself) and reads ~0, split_ms covers both split
- * launches, combine_ms the combine.
+ * HIP events around its launches on its stream: split_ms brackets the split
+ * kernel's main launch, rerun_ms the exact-max rerun launch, combine_ms the
+ * combine (0 when no combine runs).
  * mla_timing_read() synchronises on those events and returns the summed
  * milliseconds and the number of calls since the last read (then resets).
  * Up to 4096 calls are recorded between reads; later ones are not timed.
  */
 int mla_timing_enable(int enable);
-int mla_timing_read(float* plan_ms, float* split_ms, float* combine_ms, int32_t* calls);
+int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t* calls);
 
 #ifdef __cplusplus
 }

@@ -176,6 +176,7 @@ constexpr int kRopeBytes = kTileRows * 128;        // 4096
 constexpr int kTileBytes = kLatBytes + kRopeBytes; // 36864
 constexpr int kStages = 4;                         // LDS ring of tiles (144 KiB)
 constexpr int kLoadsPerTile = 9;                   // DMA instructions per wave per tile
+constexpr int kXcds = 8;                           // accelerator complex dies, each with its own L2
 constexpr int kQRegSteps = 32;                     // Q k-steps held in VGPRs (the latent part)
 constexpr int kQLdsBytes = 4 * 4 * 1024;           // RoPE k-steps of Q: [step][wave][lane] x 16 B
 static_assert(kStages * kTileBytes + kQLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
@@ -648,7 +649,22 @@ void split_kernel(SplitParams p) {
   lds_char* lds = (lds_char*)lds_raw;
   lds_char* qlds = lds + kStages * kTileBytes;
 
-  const int wi = blockIdx.x;
+  // Workgroup -> (work item, head group).  The dispatcher deals workgroups to
+  // the 8 XCDs round-robin by flat id; this bijection gives each XCD a
+  // contiguous run of (work item, head group) pairs in work-item-major order,
+  // so that the splits of a sequence share one L2 for their queries, and the
+  // head groups of a work item its cache rows.
+  int wi, hg;
+  {
+    const int ng = gridDim.y;
+    const int total = gridDim.x * ng;
+    const int flat = blockIdx.x + blockIdx.y * gridDim.x;
+    const int xcd = flat & (kXcds - 1), idx = flat / kXcds;
+    const int q = total / kXcds, r = total % kXcds;
+    const int lin = xcd * q + min(xcd, r) + idx;
+    wi = lin / ng;
+    hg = lin - wi * ng;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 31;
@@ -663,7 +679,7 @@ void split_kernel(SplitParams p) {
     split_range(clamp_len(p.seqlens[b], p.row_cap), p.num_split, k, &r0, &r1);
     s_b = p.num_split;
   } else if (!REDO) {
-    const WorkItem it = plan_item(p, wi, lane, wi == 0 && blockIdx.y == 0 && wave == 0);
+    const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
     if (!it.valid) return;
     b = it.b;
     r0 = it.r0;
@@ -686,7 +702,7 @@ void split_kernel(SplitParams p) {
 
   // Heads of this wave.  Lanes past the last head compute with a zero query
   // and write nothing.
-  const int h0 = blockIdx.y * kHeadsPerGroup + wave * 32;
+  const int h0 = hg * kHeadsPerGroup + wave * 32;
   const bool head_ok = h0 + hl < p.heads;
   const int h = head_ok ? h0 + hl : p.heads - 1;
 

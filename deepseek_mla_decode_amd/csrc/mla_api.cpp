@@ -40,7 +40,7 @@ std::atomic<int32_t> g_num_cus[kMaxDevices];
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: [plan ints][redo flags][partial lse fp32][partial out fp32].
+// Workspace layout: [plan ints][rerun flags, one per (work item, head group)][partial lse fp32][partial out fp32].
 struct Layout {
   size_t num_splits, split_offset, work, redo, part_lse, part_o, total;
 };
@@ -52,7 +52,7 @@ Layout layout(const mla_desc* d, int32_t max_work) {
   L.split_offset = L.num_splits + B * 4;
   L.work = L.split_offset + (B + 1) * 4;
   L.redo = L.work + 4 * W * 4;
-  L.part_lse = round_up(L.redo + W * 4, 256);
+  L.part_lse = round_up(L.redo + W * (size_t)mla::head_groups(d->heads) * 4, 256);
   L.part_o = round_up(L.part_lse + W * H * 4, 256);
   L.total = round_up(L.part_o + W * H * 512 * 4, 256);
   return L;

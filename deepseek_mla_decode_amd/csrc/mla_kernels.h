@@ -18,7 +18,7 @@ struct SplitParams {
   int32_t* num_splits;          // planner mode: written by workgroup 0 for the combine
   int32_t* split_offset;        // planner mode: [B + 1], written by workgroup 0
   int32_t* work;                // planner mode: work list (4 ints per item), written by workgroup 0
-  int32_t* redo;                // [max_work]: main pass overflowed, rerun with the exact max
+  int32_t* redo;                // [max_work][head groups]: main pass overflowed, rerun with the exact max
   uint16_t* out;
   float* lse;
   float* part_o;                // [max_work, H, 512]

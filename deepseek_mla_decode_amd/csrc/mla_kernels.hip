@@ -671,6 +671,11 @@ void split_kernel(SplitParams p) {
   const int g = lane >> 5;
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
+  // Rerun flag of this (work item, head group).  The main pass writes it for
+  // every workgroup of its grid; the rerun launch leaves at once when it is 0.
+  int32_t* const redo_flag = p.redo + (wi * (int)gridDim.y + hg);
+  if (REDO && *redo_flag == 0) return;
+
   // ---- work item (uniform) -------------------------------------------------
   int b, r0, r1, s_b;
   if (p.num_split > 0) {
@@ -680,20 +685,21 @@ void split_kernel(SplitParams p) {
     s_b = p.num_split;
   } else if (!REDO) {
     const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
-    if (!it.valid) return;
+    if (!it.valid) {   // past the end of the plan
+      if (threadIdx.x == 0) *redo_flag = 0;
+      return;
+    }
     b = it.b;
     r0 = it.r0;
     r1 = it.r1;
     s_b = it.s_b;
   } else {
-    // The plan the main pass published.
-    if (wi >= p.split_offset[p.batch]) return;
+    // The plan the main pass published (the flag was set, so wi is in it).
     b = p.work[4 * wi + 0];
     r0 = p.work[4 * wi + 2];
     r1 = p.work[4 * wi + 3];
     s_b = p.split_offset[b + 1] - p.split_offset[b];
   }
-  if (REDO && p.redo[wi] == 0) return;
   b = __builtin_amdgcn_readfirstlane(b);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
@@ -757,7 +763,7 @@ void split_kernel(SplitParams p) {
   // lse = -inf (or a zero partial, lse = -inf) and leaves before the
   // accumulator exists, so that it has a single definition path.
   if (n_tiles == 0) {
-    if (!REDO && threadIdx.x == 0) p.redo[wi] = 0;
+    if (!REDO && threadIdx.x == 0) *redo_flag = 0;
     if (REDO || !head_ok) return;
     if (s_b == 1) {
       uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 4 * g;
@@ -974,11 +980,11 @@ void split_kernel(SplitParams p) {
     __syncthreads();
     const bool overflow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
     if (overflow) {
-      if (wave == 0 && lane_t == 0) p.redo[wi] = 1;
+      if (wave == 0 && lane_t == 0) *redo_flag = 1;
       if (head_ok_t && g_t == 0) p.part_lse[(int64_t)wi * p.heads + h_t] = mx;
       return;
     }
-    if (wave == 0 && lane_t == 0) p.redo[wi] = 0;
+    if (wave == 0 && lane_t == 0) *redo_flag = 0;
   }
 
   // ---- epilogue: normalise; write final output or the split partial --------

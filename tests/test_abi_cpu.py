@@ -151,7 +151,7 @@ def test_workspace_size_formula(L):
         n = ctypes.c_size_t()
         assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0
         r = lambda x: -(-x // 256) * 256  # noqa: E731
-        plan = 4 * B + 4 * (B + 1) + 16 * want_w + 4 * want_w
+        plan = 4 * B + 4 * (B + 1) + 16 * want_w + 4 * want_w * hg
         part_lse = r(plan)
         part_o = r(part_lse + 4 * want_w * H)
         assert n.value == r(part_o + 2048 * want_w * H)

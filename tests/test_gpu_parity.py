@@ -275,3 +275,29 @@ def test_split_kernel_publishes_the_host_plan(mla, B):
     for b in samples:
         ro, rl = oracle.mla_decode_ref(inp, batches=[b])
         assert_parity(from_device(out)[b:b + 1], from_device(lse)[b:b + 1], ro, rl, f"B={B} seq {b}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rerun_flag_is_per_head_group(mla, dtype):
+    """256 heads (two head groups of 128): a dominant key that only heads
+    0..127 see overflows group 0 alone.  Each (work item, head group) has its
+    own rerun flag; with a shared one, group 1's 'no overflow' could hide group
+    0's and leave its output unwritten (the buffer starts as NaN here)."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    lens = [3100, 700]
+    inp = mi.make_contiguous(2, 256, 3100, lens, dtype, seed=111)
+    one = np.float16(1.0) if dtype == "f16" else mi.f32_to_bf16_bits(np.float32([1.0]))[0]
+    inp.q_pe[:] = 0
+    inp.q_pe[:, :128, :] = one
+    for b, row in ((0, 3000), (1, 650)):
+        inp.k_pe[b, row, 0, :] = mi.cast_storage(np.full(64, 30.0, dtype=np.float32), dtype)
+    d = to_device(inp, "cuda")
+    ro, rl = oracle.mla_decode_ref(inp)
+    for ns in (0, 1, 3):
+        out = torch.full((2, 256, 512), float("nan"), dtype=d["q_nope"].dtype, device="cuda")
+        lse = torch.full((2, 256), float("nan"), dtype=torch.float32, device="cuda")
+        mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"],
+                       inp.softmax_scale, num_split=ns, out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert_parity(from_device(out), from_device(lse), ro, rl, f"two head groups {dtype} split={ns}")

@@ -301,3 +301,44 @@ def test_rerun_flag_is_per_head_group(mla, dtype):
                        inp.softmax_scale, num_split=ns, out=out, lse=lse)
         torch.cuda.synchronize()
         assert_parity(from_device(out), from_device(lse), ro, rl, f"two head groups {dtype} split={ns}")
+
+
+@pytest.mark.parametrize("page", [256, 512])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_paged_large_pages(mla, page, dtype):
+    """Pages of 256 and 512 rows: a 32-row tile never straddles a page, and
+    splits start and end inside pages."""
+    lens = [1, 255, 256, 257, 1100, 2049]
+    inp = mi.make_paged(len(lens), 128, lens, dtype, seed=112, page_block_size=page, spare_pages=2)
+    ro, rl = oracle.mla_decode_ref(inp)
+    for ns in (0, 3, 7):
+        out, lse = _run(mla, inp, ns)
+        assert_parity(out, lse, ro, rl, f"paged page={page} {dtype} split={ns}")
+
+
+def test_paged_two_head_groups(mla):
+    """256 heads over a paged cache with the planner: two workgroups share each
+    work item's cache rows."""
+    lens = [900, 40, 2500]
+    inp = mi.make_paged(len(lens), 256, lens, "bf16", seed=113, page_block_size=64, spare_pages=4)
+    ro, rl = oracle.mla_decode_ref(inp)
+    for ns in (0, 2):
+        out, lse = _run(mla, inp, ns)
+        assert_parity(out, lse, ro, rl, f"paged H=256 split={ns}")
+
+
+def test_lengths_beyond_the_cache_are_clamped(mla):
+    """A contiguous cache of 100 rows per sequence with lengths 150 and 100:
+    the kernel clamps lengths to the cache, so both sequences give the result
+    of their first 100 rows."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    inp = mi.make_contiguous(2, 128, 100, [100, 100], "f16", seed=114)
+    d = to_device(inp, "cuda")
+    lens = torch.tensor([150, 100], dtype=torch.int32, device="cuda")
+    for ns in (0, 1, 2):
+        out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, lens,
+                                  inp.softmax_scale, num_split=ns)
+        torch.cuda.synchronize()
+        ro, rl = oracle.mla_decode_ref(inp)
+        assert_parity(from_device(out), from_device(lse), ro, rl, f"clamped split={ns}")

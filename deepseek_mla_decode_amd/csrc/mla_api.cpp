@@ -87,21 +87,35 @@ int max_work_of(const mla_desc* d, int32_t num_split, int32_t num_cus, int32_t* 
 
 // ---- timing ----------------------------------------------------------------
 constexpr int kMaxTimed = 4096;
+constexpr int kEventsPerCall = 6;
 std::mutex g_tmu;
 bool g_timing = false;
-std::vector<hipEvent_t> g_events;  // 4 per call
+std::vector<hipEvent_t> g_events;  // 6 per call: split, rerun, combine (start, stop)
+std::vector<uint8_t> g_combined;   // per call: whether a combine ran (and its events were recorded)
 int g_timed = 0;
 
-hipEvent_t* timing_slot() {
+// A timed call's events (copies of the handles, so that another thread
+// growing the pool cannot invalidate them) and its index.
+struct TimingSlot {
+  int index;
+  hipEvent_t ev[kEventsPerCall];
+};
+
+bool timing_slot(TimingSlot* s) {
   std::lock_guard<std::mutex> lk(g_tmu);
-  if (!g_timing || g_timed >= kMaxTimed) return nullptr;
-  const size_t need = 4 * (size_t)(g_timed + 1);
+  if (!g_timing || g_timed >= kMaxTimed) return false;
+  const size_t need = kEventsPerCall * (size_t)(g_timed + 1);
   while (g_events.size() < need) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return false;
     g_events.push_back(e);
   }
-  return &g_events[4 * (size_t)g_timed++];
+  if (g_combined.size() < (size_t)g_timed + 1) g_combined.resize((size_t)g_timed + 1);
+  g_combined[g_timed] = 0;
+  s->index = g_timed;
+  for (int k = 0; k < kEventsPerCall; ++k) s->ev[k] = g_events[kEventsPerCall * (size_t)g_timed + k];
+  ++g_timed;
+  return true;
 }
 
 }  // namespace
@@ -317,18 +331,17 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.row_cap = row_cap;
   sp.num_cus = num_cus;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipEvent_t* ev = timing_slot();
-  if (ev) (void)hipEventRecord(ev[0], stream);
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream)) !=
-      hipSuccess)
+  // Timing (when enabled): each launch is timed from its dispatch packet.
+  TimingSlot ts;
+  hipEvent_t* ev = timing_slot(&ts) ? ts.ev : nullptr;
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream,
+                             ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
-  if (ev) (void)hipEventRecord(ev[1], stream);
   // Work items whose main pass overflowed the P range are redone with their
   // exact max; every other workgroup of this launch exits at once.
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), true, stream)) !=
-      hipSuccess)
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), true, stream,
+                             ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "redo launch: %s", hipGetErrorString(e));
-  if (ev) (void)hipEventRecord(ev[2], stream);
 
   if (num_split != 1) {
     mla::CombineParams cp{};
@@ -343,10 +356,14 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     cp.heads = d->heads;
     // Splits per sequence on average: forced, or at most max_work / B.
     const int mean_splits = num_split > 0 ? num_split : (max_work + d->batch - 1) / (d->batch > 0 ? d->batch : 1);
-    if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream)) != hipSuccess)
+    if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream, ev ? ev[4] : nullptr,
+                                 ev ? ev[5] : nullptr)) != hipSuccess)
       return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    if (ev) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      g_combined[ts.index] = 1;
+    }
   }
-  if (ev) (void)hipEventRecord(ev[3], stream);
   return ok();
 }
 
@@ -362,12 +379,13 @@ int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t
   std::lock_guard<std::mutex> lk(g_tmu);
   double acc[3] = {0, 0, 0};
   for (int i = 0; i < g_timed; ++i) {
-    hipEvent_t* ev = &g_events[4 * (size_t)i];
-    hipError_t e = hipEventSynchronize(ev[3]);
+    hipEvent_t* ev = &g_events[kEventsPerCall * (size_t)i];
+    const int launches = g_combined[i] ? 3 : 2;
+    hipError_t e = hipEventSynchronize(ev[2 * launches - 1]);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < launches; ++k) {
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, ev[k], ev[k + 1]);
+      e = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]);
       if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
       acc[k] += ms;
     }

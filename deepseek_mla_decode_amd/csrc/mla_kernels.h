@@ -56,11 +56,13 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+// t0 / t1: events that time the launch from its dispatch packet, or null.
 hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
-                        hipStream_t stream);
+                        hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // mean_splits: splits per sequence, on average (forced count, or the plan's
 // bound over the batch); from kCombineSplitkMin on, four waves share a head.
 constexpr int kCombineSplitkMin = 16;
-hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream,
+                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 }  // namespace mla

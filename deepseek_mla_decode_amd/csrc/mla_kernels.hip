@@ -45,6 +45,8 @@
 #include "plan_rule.h"
 #include "mla_kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace mla {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -1273,36 +1275,47 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// A launch, timed from its dispatch packet when events are given (as a
+// profiler times it, without the latency of separate event packets).
+template <typename Kernel, typename Params>
+static void launch_k(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t t0, hipEvent_t t1,
+                     const Params& p) {
+  if (t0) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t0, t1, 0, p);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+}
+
 template <bool REDO>
-static void launch_split_t(const SplitParams& p, int dtype, bool paged, dim3 grid, hipStream_t stream) {
+static void launch_split_t(const SplitParams& p, int dtype, bool paged, dim3 grid, hipStream_t stream,
+                           hipEvent_t t0, hipEvent_t t1) {
   const dim3 block(kThreads);
   if (dtype == MLA_DTYPE_F16) {
-    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, true, REDO>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_F16, false, REDO>), grid, block, 0, stream, p);
+    if (paged) launch_k(split_kernel<MLA_DTYPE_F16, true, REDO>, grid, block, stream, t0, t1, p);
+    else launch_k(split_kernel<MLA_DTYPE_F16, false, REDO>, grid, block, stream, t0, t1, p);
   } else {
-    if (paged) hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, true, REDO>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_kernel<MLA_DTYPE_BF16, false, REDO>), grid, block, 0, stream, p);
+    if (paged) launch_k(split_kernel<MLA_DTYPE_BF16, true, REDO>, grid, block, stream, t0, t1, p);
+    else launch_k(split_kernel<MLA_DTYPE_BF16, false, REDO>, grid, block, stream, t0, t1, p);
   }
 }
 
 hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid(grid_x, grid_y);
-  if (redo) launch_split_t<true>(p, dtype, paged, grid, stream);
-  else launch_split_t<false>(p, dtype, paged, grid, stream);
+  if (redo) launch_split_t<true>(p, dtype, paged, grid, stream, t0, t1);
+  else launch_split_t<false>(p, dtype, paged, grid, stream, t0, t1);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream) {
+hipError_t launch_combine(const CombineParams& p, int dtype, int batch, int mean_splits, hipStream_t stream,
+                          hipEvent_t t0, hipEvent_t t1) {
   const dim3 block(256);
   if (mean_splits >= kCombineSplitkMin) {
     const dim3 grid(p.heads, batch);
-    if (dtype == MLA_DTYPE_F16) hipLaunchKernelGGL(combine_splitk_kernel<MLA_DTYPE_F16>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(combine_splitk_kernel<MLA_DTYPE_BF16>, grid, block, 0, stream, p);
+    if (dtype == MLA_DTYPE_F16) launch_k(combine_splitk_kernel<MLA_DTYPE_F16>, grid, block, stream, t0, t1, p);
+    else launch_k(combine_splitk_kernel<MLA_DTYPE_BF16>, grid, block, stream, t0, t1, p);
   } else {
     const dim3 grid((p.heads + 3) / 4, batch);
-    if (dtype == MLA_DTYPE_F16) hipLaunchKernelGGL(combine_heads_kernel<MLA_DTYPE_F16>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(combine_heads_kernel<MLA_DTYPE_BF16>, grid, block, 0, stream, p);
+    if (dtype == MLA_DTYPE_F16) launch_k(combine_heads_kernel<MLA_DTYPE_F16>, grid, block, stream, t0, t1, p);
+    else launch_k(combine_heads_kernel<MLA_DTYPE_BF16>, grid, block, stream, t0, t1, p);
   }
   return hipGetLastError();
 }

@@ -192,10 +192,11 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
 const char* mla_last_error(void);
 
 /*
- * Kernel timing for measurement.  While enabled, every mla_decode call records
- * HIP events around its launches on its stream: split_ms brackets the split
- * kernel's main launch, rerun_ms the exact-max rerun launch, combine_ms the
- * combine (0 when no combine runs).
+ * Kernel timing for measurement.  While enabled, every mla_decode call times
+ * its launches on its stream from their dispatch packets (start and stop
+ * events of the launch itself): split_ms the split kernel's main launch,
+ * rerun_ms the exact-max rerun launch, combine_ms the combine (0 when no
+ * combine runs).
  * mla_timing_read() synchronises on those events and returns the summed
  * milliseconds and the number of calls since the last read (then resets).
  * Up to 4096 calls are recorded between reads; later ones are not timed.

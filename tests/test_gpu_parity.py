@@ -342,3 +342,24 @@ def test_lengths_beyond_the_cache_are_clamped(mla):
         torch.cuda.synchronize()
         ro, rl = oracle.mla_decode_ref(inp)
         assert_parity(from_device(out), from_device(lse), ro, rl, f"clamped split={ns}")
+
+
+def test_timing_reports_each_launch(mla):
+    """mla_timing_read: per-launch times from the launches' own dispatch
+    events; the combine bracket is empty when a single split writes out."""
+    import torch
+    from mla_inputs.torch_io import to_device
+    inp = mi.make_config(0)
+    d = to_device(inp, "cuda")
+    args = (d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"], inp.softmax_scale)
+    for ns, has_combine in ((4, True), (1, False)):
+        mla.mla_timing_enable(True)
+        mla.mla_timing_read()
+        for _ in range(3):
+            mla.mla_decode(*args, num_split=ns)
+        torch.cuda.synchronize()
+        split_ms, rerun_ms, comb_ms, calls = mla.mla_timing_read()
+        mla.mla_timing_enable(False)
+        assert calls == 3
+        assert 0 < split_ms < 1000 and 0 <= rerun_ms < 1000
+        assert (comb_ms > 0) == has_combine and comb_ms < 1000

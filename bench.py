@@ -10,9 +10,9 @@ inputs, softmax_scale = 1/sqrt(576), planner-chosen splits.
 Prints ONE JSON line.  Throughput is TFLOPS of the algorithmic work
 2·H·(576 + 512) per valid cache row; the line also carries KV GB/s, µs per
 call, the fraction of the per-workload roofline min(8 TB/s × intensity, 2.5
-PFLOP/s dense fp16/bf16), per-kernel timing of the split kernel from HIP events
-(`roofline`), and the fp64 CPU oracle timed on a bounded sample
-(`cpu_baseline`).
+PFLOP/s dense fp16/bf16), the split kernel's launch time (from the launch's own
+dispatch events) against the HBM peak with its measured traffic (`roofline`),
+and the fp64 CPU oracle timed on a sample of the workload (`cpu_baseline`).
 """
 from __future__ import annotations
 

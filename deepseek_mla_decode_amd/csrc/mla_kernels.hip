@@ -1,11 +1,16 @@
 // mla_kernels.hip -- gfx950 (CDNA4) kernels of the MLA decode library.
 //
-// Three kernels:
-//   * plan_kernel    one workgroup; turns cache_seqlens into the split plan.
+// Kernels:
+//   * plan_kernel    one workgroup; turns cache_seqlens into the split plan
+//                    (the stand-alone planner entry point; decode itself plans
+//                    inside split_kernel, every wave for its own work item).
 //   * split_kernel   one workgroup per (work item, head group of 128 heads);
 //                    streams the work item's KV rows through LDS and runs the
-//                    base-2 online softmax with both products on MFMA.
-//   * combine_kernel merges the per-split partials of sequences with s_b > 1.
+//                    base-2 online softmax with both products on MFMA.  Its
+//                    REDO instance reruns the items whose fixed max fell short.
+//   * combine_heads_kernel / combine_splitk_kernel merge the per-split
+//                    partials of sequences with s_b > 1: one wave per head for
+//                    few splits, four waves over the splits of a head for many.
 //
 // What is computed follows the TileLang MLA guide ("用 TileLang 编写高性能
 // DeepSeek MLA 内核"): "Split Kernel" (score tile = q_nope·latentᵀ + q_pe·ropeᵀ
@@ -1033,18 +1038,32 @@ void split_kernel(SplitParams p) {
 // final LSE from all split lse values first, then the weighted sum.
 // ---------------------------------------------------------------------------
 
+// Float max / sum over a wave: DPP within each row of 16 lanes, then the four
+// row results read out (the result is wave-uniform).
+template <int CTRL>
+__device__ __forceinline__ float mov_dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, mov_dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, mov_dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, mov_dpp_f32<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, mov_dpp_f32<0x140>(v));   // row_mirror
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += mov_dpp_f32<0xB1>(v);
+  v += mov_dpp_f32<0x4E>(v);
+  v += mov_dpp_f32<0x141>(v);
+  v += mov_dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
-constexpr int kCombineUnroll = 8;   // splits per wave whose reads are in flight together
+constexpr int kCombineUnroll = 8;   // splits per wave whose reads are in flight together (one wave per head)
+constexpr int kSplitkBatch = 16;    // the same for each of the four waves of a head
 
 // Number of splits of sequence b and its first work item.
 __device__ __forceinline__ void combine_range(const CombineParams& p, int b, int& s, int& base) {
@@ -1057,6 +1076,97 @@ __device__ __forceinline__ void combine_range(const CombineParams& p, int b, int
   }
 }
 
+// Final base-2 lse of a head from the split lse values held two per lane
+// (l0 of split lane, l1 of split lane + 64; -inf past the splits) plus any
+// splits beyond the first 128, and this lane's weight for split `lane`.  A head
+// whose splits are all empty gets total = -inf and weight 0 everywhere
+// (output 0, lse -inf), without a branch, so that the partial-row reads
+// already in flight stay in flight.
+struct CombineWeights {
+  float total, w_own;
+};
+__device__ __forceinline__ CombineWeights combine_weights(float l0, float l1, const float* L, int heads, int s,
+                                                          int lane) {
+  float mx = fmaxf(l0, l1);
+  for (int k = lane + 128; k < s; k += 64) mx = fmaxf(mx, L[(int64_t)k * heads]);
+  mx = wave_max(mx);
+  const float ref = mx == -__builtin_inff() ? 0.f : mx;
+  float se = __builtin_amdgcn_exp2f(l0 - ref) + __builtin_amdgcn_exp2f(l1 - ref);   // 0 past s
+  for (int k = lane + 128; k < s; k += 64) se += __builtin_amdgcn_exp2f(L[(int64_t)k * heads] - ref);
+  se = wave_sum(se);
+  const float total = __log2f(se) + ref;   // -inf when every split is empty
+  const float w_own = se > 0.f ? __builtin_amdgcn_exp2f(l0 - total) : 0.f;
+  return {total, w_own};
+}
+
+// lse of split k = lane + 64 j as held by the lane (-inf past s), read without
+// a branch: lanes past s re-read split s - 1.
+__device__ __forceinline__ float lane_lse(const float* L, int heads, int s, int k) {
+  const float l = L[(int64_t)(k < s ? k : s - 1) * heads];
+  return k < s ? l : -__builtin_inff();
+}
+
+// One wave merges the s splits of head h of sequence b; lane l owns output
+// columns 8 l .. 8 l + 7.  S = s when s is 2..kCombineUnroll (every read of
+// the partial rows issued before the first wait), S = 0 for any larger count.
+template <int DT, int S>
+__device__ __forceinline__ void combine_head(const CombineParams& p, int b, int h, int lane, int s_rt, int base) {
+  constexpr int U = S ? S : kCombineUnroll;
+  const int s = S ? S : s_rt;
+  const float* L = p.part_lse + (int64_t)base * p.heads + h;
+  const int64_t stride = (int64_t)p.heads * 512;   // floats between consecutive splits
+  const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
+  // Lane k holds the lse of split k (and k + 64).  The first U partial rows
+  // are read in the same round trip: they do not depend on the weights.
+  const float l0 = lane_lse(L, p.heads, s, lane);
+  const float l1 = S ? -__builtin_inff() : lane_lse(L, p.heads, s, lane + 64);
+  f32x4 v0[U], v1[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)u * stride);
+    v0[u] = src[0];
+    v1[u] = src[1];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
+  const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float w = lane_f32(cw.w_own, u);   // split u's weight, held by lane u
+    a0 += w * v0[u];
+    a1 += w * v1[u];
+  }
+  if constexpr (S == 0) {
+    // s > U: further batches of U; indices past s re-read split s - 1 with weight 0.
+    const bool any = cw.total != -__builtin_inff();
+    for (int k0 = U; k0 < s; k0 += U) {
+      float lk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u < s ? k0 + u : s - 1;
+        const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
+        v0[u] = src[0];
+        v1[u] = src[1];
+        lk[u] = L[(int64_t)k * p.heads];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = any && k0 + u < s ? __builtin_amdgcn_exp2f(lk[u] - cw.total) : 0.f;
+        a0 += w * v0[u];
+        a1 += w * v1[u];
+      }
+    }
+  }
+  u32x4 r;
+  r.x = pack2<DT>(a0.x, a0.y);
+  r.y = pack2<DT>(a0.z, a0.w);
+  r.z = pack2<DT>(a1.x, a1.y);
+  r.w = pack2<DT>(a1.z, a1.w);
+  uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 8 * lane;
+  *reinterpret_cast<u32x4*>(o) = r;
+  if (lane == 0) p.lse[(int64_t)b * p.heads + h] = cw.total * kLn2;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
   const int b = blockIdx.y;
@@ -1065,44 +1175,25 @@ __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
   if (h >= p.heads) return;
   int s, base;
   combine_range(p, b, s, base);
-  if (s <= 1) return;
-
-  const float* L = p.part_lse + (int64_t)base * p.heads + h;
-  float mx = -__builtin_inff();
-  for (int k = lane; k < s; k += 64) mx = fmaxf(mx, L[(int64_t)k * p.heads]);
-  mx = wave_max(mx);
-
-  uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 8 * lane;
-  if (mx == -__builtin_inff()) {
-    *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
-    if (lane == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
-    return;
+  static_assert(kCombineUnroll == 8, "the cases below list 2..kCombineUnroll");
+  switch (s) {
+    case 0:
+    case 1: return;   // one split wrote out/lse itself
+    case 2: combine_head<DT, 2>(p, b, h, lane, s, base); break;
+    case 3: combine_head<DT, 3>(p, b, h, lane, s, base); break;
+    case 4: combine_head<DT, 4>(p, b, h, lane, s, base); break;
+    case 5: combine_head<DT, 5>(p, b, h, lane, s, base); break;
+    case 6: combine_head<DT, 6>(p, b, h, lane, s, base); break;
+    case 7: combine_head<DT, 7>(p, b, h, lane, s, base); break;
+    case 8: combine_head<DT, 8>(p, b, h, lane, s, base); break;
+    default: combine_head<DT, 0>(p, b, h, lane, s, base); break;
   }
-  float se = 0.f;
-  for (int k = lane; k < s; k += 64) se += __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - mx);
-  se = wave_sum(se);
-  const float total = __log2f(se) + mx;
-
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
-  for (int k = 0; k < s; ++k) {
-    const float w = __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - total);
-    const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * p.heads * 512);
-    a0 += w * src[0];
-    a1 += w * src[1];
-  }
-  u32x4 r;
-  r.x = pack2<DT>(a0.x, a0.y);
-  r.y = pack2<DT>(a0.z, a0.w);
-  r.z = pack2<DT>(a1.x, a1.y);
-  r.w = pack2<DT>(a1.z, a1.w);
-  *reinterpret_cast<u32x4*>(o) = r;
-  if (lane == 0) p.lse[(int64_t)b * p.heads + h] = total * kLn2;
 }
 
-// Wave w accumulates splits w, w + 4, ... (8 output values per lane, eight
-// splits' reads in flight); the four sums meet in LDS, and wave w writes
-// output columns 128 w .. 128 w + 127.
+// Wave w accumulates splits w, w + 4, ... in batches of kSplitkBatch (8
+// output values per lane; a batch's partial rows and lse values are read
+// together, the first batch before the final lse is known); the four sums meet
+// in LDS, and wave w writes output columns 128 w .. 128 w + 127.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   __shared__ f32x4 red[4][2][64];   // [wave][half][lane]: 8 values per lane
@@ -1110,52 +1201,43 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int s, base;
   combine_range(p, b, s, base);
-  if (s <= 1) return;   // uniform: one split wrote out/lse itself
+  if (s <= 1) return;   // one split wrote out/lse itself
 
+  constexpr int U = kSplitkBatch;
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
-  float mx = -__builtin_inff();
-  for (int k = lane; k < s; k += 64) mx = fmaxf(mx, L[(int64_t)k * p.heads]);
-  mx = wave_max(mx);
-  if (mx == -__builtin_inff()) {   // every split empty
-    if (wave == 0) {
-      uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 8 * lane;
-      *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
-      if (lane == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
-    }
-    return;
-  }
-  float se = 0.f;
-  for (int k = lane; k < s; k += 64) se += __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - mx);
-  se = wave_sum(se);
-  const float total = __log2f(se) + mx;
-
-  // This wave's splits: k = wave + 4 i.
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   const int64_t stride = (int64_t)p.heads * 512;   // floats between consecutive splits
   const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
-  int k = wave;
-  for (; k + 4 * (kCombineUnroll - 1) < s; k += 4 * kCombineUnroll) {
-    f32x4 v0[kCombineUnroll], v1[kCombineUnroll];
-    float w[kCombineUnroll];
+  const float l0 = lane_lse(L, p.heads, s, lane), l1 = lane_lse(L, p.heads, s, lane + 64);
+  // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
+  // s re-read split s - 1, which then gets weight 0.
+  f32x4 v0[U], v1[U];
+  float lk[U];
+  auto load_batch = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)(k + 4 * u) * stride);
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
+      const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
       v0[u] = src[0];
       v1[u] = src[1];
-      w[u] = L[(int64_t)(k + 4 * u) * p.heads];
+      lk[u] = L[(int64_t)k * p.heads];
     }
+  };
+  load_batch(wave);
+  __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
+  const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
+  const bool any = cw.total != -__builtin_inff();
+
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = wave;;) {
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      const float wu = __builtin_amdgcn_exp2f(w[u] - total);
-      a0 += wu * v0[u];
-      a1 += wu * v1[u];
+    for (int u = 0; u < U; ++u) {
+      const float w = any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lk[u] - cw.total) : 0.f;
+      a0 += w * v0[u];
+      a1 += w * v1[u];
     }
-  }
-  for (; k < s; k += 4) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
-    const float wu = __builtin_amdgcn_exp2f(L[(int64_t)k * p.heads] - total);
-    a0 += wu * src[0];
-    a1 += wu * src[1];
+    k0 += 4 * U;
+    if (k0 >= s) break;
+    load_batch(k0);
   }
   red[wave][0][lane] = a0;
   red[wave][1][lane] = a1;
@@ -1172,7 +1254,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   }
   uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 128 * wave + 2 * lane;
   *reinterpret_cast<uint32_t*>(o) = pack2<DT>(c0, c1);
-  if (wave == 0 && lane == 0) p.lse[(int64_t)b * p.heads + h] = total * kLn2;
+  if (wave == 0 && lane == 0) p.lse[(int64_t)b * p.heads + h] = cw.total * kLn2;
 }
 
 // ---------------------------------------------------------------------------

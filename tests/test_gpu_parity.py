@@ -75,6 +75,38 @@ def test_ragged_lengths(mla, dtype, num_split):
     assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("num_split", [2, 3, 5, 6, 7, 8, 9, 15, 16, 17, 64, 65, 129, 130])
+def test_combine_split_counts(mla, dtype, num_split):
+    """Every shape of the combine: 2..8 splits (one wave per head, each count
+    compiled on its own), 9..15 (batches of 8), 16 and more (four waves per
+    head), beyond 64 and beyond 128 splits (the lse values past the two a lane
+    holds); the L = 0 sequence has only empty splits (out 0, lse -inf), and
+    L = 1 and 700 leave most of their splits empty."""
+    lens = [0, 1, 700, 2600]
+    inp = mi.make_contiguous(len(lens), 64, 2600, lens, dtype, seed=103)
+    out, lse = _run(mla, inp, num_split)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"combine {dtype} split={num_split}")
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+
+
+def test_planner_one_long_sequence_among_short_ones(mla):
+    """Planner mode: one sequence of 40000 rows among 63 of 64 rows.  The long
+    one gets 157 splits while the mean stays at 4, so the one-wave-per-head
+    combine meets more than 128 splits."""
+    lens = [40000] + [64] * 63
+    inp = mi.make_paged(len(lens), 128, lens, "bf16", seed=104, page_block_size=64)
+    cus = mla.mla_num_cus(0)
+    nsa, _, _ = mla.mla_plan_host(np.asarray(lens, np.int32), 128, 0, cus)
+    if int(nsa[0]) <= 128:
+        pytest.skip(f"{cus} CUs give the long sequence only {int(nsa[0])} splits")
+    out, lse = _run(mla, inp, 0)
+    for b in (0, 1, 63):
+        ro, rl = oracle.mla_decode_ref(inp, batches=[b])
+        assert_parity(out[b:b + 1], lse[b:b + 1], ro, rl, f"long among short, seq {b}")
+
+
 @pytest.mark.parametrize("heads", [1, 16, 33, 96, 128, 160, 256])
 def test_head_counts(mla, heads):
     inp = mi.make_contiguous(3, heads, 150, [150, 77, 5], "f16", seed=102)

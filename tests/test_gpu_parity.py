@@ -310,6 +310,86 @@ def test_split_kernel_publishes_the_host_plan(mla, B):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_many_short_sequences_with_reruns(mla, dtype):
+    """Planner mode, 120 short sequences (some split, some not, two empty).
+    The RoPE part of 2% of the keys is scaled by 64 (fp16) or 256 (bf16):
+    their scores rise far above most splits' first tiles, so the rerun launch
+    redoes most splits, of single-split and multi-split sequences alike.  V
+    (the latent part) stays N(0,1), so the fp16/bf16 rounding of P stays
+    within the tolerance; every sequence is checked."""
+    rng = np.random.default_rng(31)
+    B = 120
+    lens = rng.integers(40, 700, size=B)
+    lens[[3, 77]] = 0
+    inp = mi.make_contiguous(B, 128, 700, lens, dtype, seed=111)
+    factor = 64.0 if dtype == "f16" else 256.0
+    for b in range(B):
+        for j in rng.choice(int(lens[b]), size=int(round(0.02 * lens[b])), replace=False):
+            inp.k_pe[b, j, 0] = mi._scaled(inp.k_pe[b, j, 0], factor, dtype)
+    nsa, _, _ = mla.mla_plan_host(np.asarray(lens, np.int32), 128, 0, mla.mla_num_cus(0))
+    assert (nsa > 1).any() and (nsa == 1).any()
+    out, lse = _run(mla, inp, 0)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"many short sequences, reruns, {dtype}")
+
+
+@pytest.mark.parametrize("dtype,boost", [("f16", False), ("bf16", True)])
+def test_graph_replay_matches_eager(mla, dtype, boost):
+    """One decode call captured in a HIP graph, replayed four times with eager
+    work in between (the outputs overwritten, an eager call on other inputs
+    through the same workspace): every replay equals the eager result bit for
+    bit.  With `boost`, keys whose RoPE part is scaled by 256 make splits
+    overflow, so the rerun launch inside the graph does work too."""
+    import torch
+    from mla_inputs.torch_io import to_device
+    lens = [900, 1, 0, 450, 777, 64, 65, 300]
+    inp = mi.make_contiguous(len(lens), 128, 900, lens, dtype, seed=120)
+    if boost:
+        rng = np.random.default_rng(3)
+        for b, L in enumerate(lens):
+            for j in rng.choice(L, size=L // 50, replace=False):
+                inp.k_pe[b, j, 0] = mi._scaled(inp.k_pe[b, j, 0], 256.0, dtype)
+    other = mi.make_contiguous(len(lens), 128, 900, lens[::-1], dtype, seed=121)
+    d, d2 = to_device(inp, "cuda"), to_device(other, "cuda")
+    tdt = d["q_nope"].dtype
+    out = torch.empty((len(lens), 128, 512), dtype=tdt, device="cuda")
+    lse = torch.empty((len(lens), 128), dtype=torch.float32, device="cuda")
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, out)
+    ws = torch.empty(mla.mla_workspace_size(desc, 0, mla.mla_num_cus(0)), dtype=torch.uint8, device="cuda")
+
+    def call(dd, o, l):
+        mla.mla_decode(dd["q_nope"], dd["q_pe"], dd["kv_latent"], dd["k_pe"], None, dd["cache_seqlens"],
+                       inp.softmax_scale, num_split=0, out=o, lse=l, workspace=ws)
+
+    call(d, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    ro, rl = oracle.mla_decode_ref(inp, batches=[0, 3])
+    from mla_inputs.torch_io import from_device
+    assert_parity(from_device(ref_o)[[0, 3]], from_device(ref_l)[[0, 3]], ro, rl, "eager")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        call(d, out, lse)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        call(d, out, lse)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        call(d2, out2, lse2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse.isnan(), ref_l.isnan()), f"replay {r}"
+        assert torch.equal(torch.nan_to_num(lse), torch.nan_to_num(ref_l)), f"replay {r} lse"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_rerun_flag_is_per_head_group(mla, dtype):
     """256 heads (two head groups of 128): a dominant key that only heads
     0..127 see overflows group 0 alone.  Each (work item, head group) has its

@@ -166,7 +166,10 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *   q_nope [B, H, 512], q_pe [B, H, 64]     dtype, strides in desc
  *   kv_latent, k_pe                         cache (see mla_desc)
  *   block_table  int32, NULL for a contiguous cache
- *   cache_seqlens int32[B], each >= 0 (a negative length gives undefined output)
+ *   cache_seqlens int32[B]; the lengths stay on the device, so they are
+ *                  clamped in the kernels rather than checked: a negative
+ *                  length counts as 0, and a contiguous cache's lengths are
+ *                  capped at desc->max_seqlen
  *   softmax_scale  multiplies the raw dot products (typically 1/sqrt(576));
  *                  must be finite and > 0 (MLA_ERR_INVALID_ARG otherwise)
  *   num_split  0 = planner chooses s_b per sequence; > 0 forces s_b = num_split

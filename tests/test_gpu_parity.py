@@ -456,6 +456,38 @@ def test_lengths_beyond_the_cache_are_clamped(mla):
         assert_parity(from_device(out), from_device(lse), ro, rl, f"clamped split={ns}")
 
 
+def test_max_forced_splits(mla):
+    """num_split = 1024 (the largest allowed): 70000 rows give 1024 splits of one
+    or two blocks, 5000 rows leave most of their 1024 splits empty; the combine
+    (four waves per head) then reads lse values past the 128 its lanes hold."""
+    lens = [70000, 5000]
+    inp = mi.make_contiguous(len(lens), 32, 70000, lens, "bf16", seed=131)
+    out, lse = _run(mla, inp, 1024)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, "1024 forced splits")
+
+
+def test_negative_lengths_count_as_zero(mla):
+    """cache_seqlens are device data, so the kernels clamp them instead of
+    rejecting them: a negative length behaves as 0 (out 0, lse -inf), in
+    planner mode and with forced splits, and the other sequences are untouched."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    lens = [-5, 100, -1, 0, 70]
+    inp = mi.make_contiguous(len(lens), 128, 100, [max(L, 0) for L in lens], "f16", seed=130)
+    d = to_device(inp, "cuda")
+    d["cache_seqlens"] = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for ns in (0, 1, 3):
+        out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"],
+                                  inp.softmax_scale, num_split=ns)
+        torch.cuda.synchronize()
+        out, lse = from_device(out), from_device(lse)
+        for b in (0, 2, 3):
+            assert (out[b] == 0).all() and np.isneginf(lse[b]).all(), (ns, b)
+        ro, rl = oracle.mla_decode_ref(inp, batches=[1, 4])
+        assert_parity(out[[1, 4]], lse[[1, 4]], ro, rl, f"negative lengths, split={ns}")
+
+
 def test_timing_reports_each_launch(mla):
     """mla_timing_read: per-launch times from the launches' own dispatch
     events; the combine bracket is empty when a single split writes out."""

@@ -87,7 +87,7 @@ class MlaInputs:
     """One MLA decode problem: queries, KV cache (contiguous or paged), lengths."""
 
     dtype: str
-    q_nope: np.ndarray            # [B, H, 512]
+    q_nope: np.ndarray            # [B, H, 512] (H = seqlen_q x heads per token, token-major)
     q_pe: np.ndarray              # [B, H, 64]
     cache_seqlens: np.ndarray     # int32 [B]
     softmax_scale: float
@@ -96,6 +96,7 @@ class MlaInputs:
     pool: Optional[np.ndarray] = None        # paged: [P, page, 1, 576]
     block_table: Optional[np.ndarray] = None  # paged: int32 [B, max_blocks]
     page_block_size: int = 0
+    seqlen_q: int = 1             # query tokens per sequence (rows of q are token-major)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -108,7 +109,12 @@ class MlaInputs:
 
     @property
     def heads(self) -> int:
+        """Query rows per sequence: seqlen_q x heads_per_token."""
         return self.q_nope.shape[1]
+
+    @property
+    def heads_per_token(self) -> int:
+        return self.q_nope.shape[1] // self.seqlen_q
 
 
 def default_scale() -> float:
@@ -122,27 +128,30 @@ def make_queries(ss: np.random.SeedSequence, batch: int, heads: int, dtype: str)
 
 
 def make_contiguous(batch: int, heads: int, max_seqlen: int, cache_seqlens, dtype: str = "f16",
-                    seed: int = 0, scale: Optional[float] = None) -> MlaInputs:
-    """Contiguous cache ``[B, S, 1, 512] + [B, S, 1, 64]``, all rows N(0,1)."""
+                    seed: int = 0, scale: Optional[float] = None, seqlen_q: int = 1) -> MlaInputs:
+    """Contiguous cache ``[B, S, 1, 512] + [B, S, 1, 64]``, all rows N(0,1).
+
+    With ``seqlen_q`` > 1 each sequence has that many query tokens of ``heads``
+    heads each, stored as ``seqlen_q * heads`` query rows, token-major."""
     lens = np.asarray(cache_seqlens, dtype=np.int32).reshape(batch)
     if lens.size and (lens.min() < 0 or lens.max() > max_seqlen):
         raise ValueError("cache_seqlens must lie in [0, max_seqlen]")
     root = np.random.SeedSequence(seed)
     sq, skv = root.spawn(2)
-    q_nope, q_pe = make_queries(sq, batch, heads, dtype)
+    q_nope, q_pe = make_queries(sq, batch, heads * seqlen_q, dtype)
     rows = _normal_rows(skv, batch * max_seqlen, D_QK, dtype).reshape(batch, max_seqlen, 1, D_QK)
     return MlaInputs(
         dtype=dtype, q_nope=q_nope, q_pe=q_pe, cache_seqlens=lens,
         softmax_scale=default_scale() if scale is None else float(scale),
         kv_latent=np.ascontiguousarray(rows[..., :D_LATENT]),
-        k_pe=np.ascontiguousarray(rows[..., D_LATENT:]),
+        k_pe=np.ascontiguousarray(rows[..., D_LATENT:]), seqlen_q=seqlen_q,
         meta={"layout": "contiguous", "seed": seed, "max_seqlen": max_seqlen},
     )
 
 
 def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed: int = 0,
                page_block_size: int = 64, max_blocks: Optional[int] = None, shuffle: bool = True,
-               spare_pages: int = 0, scale: Optional[float] = None) -> MlaInputs:
+               spare_pages: int = 0, scale: Optional[float] = None, seqlen_q: int = 1) -> MlaInputs:
     """Paged pool ``[P, page, 1, 576]`` with a block_table.
 
     Each sequence owns ``ceil(L_b / page)`` logical pages.  Physical pages are a
@@ -163,7 +172,7 @@ def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed:
     n_pages = n_used + spare_pages
     root = np.random.SeedSequence(seed)
     sq, skv, sperm = root.spawn(3)
-    q_nope, q_pe = make_queries(sq, batch, heads, dtype)
+    q_nope, q_pe = make_queries(sq, batch, heads * seqlen_q, dtype)
     pool = _normal_rows(skv, max(n_pages, 1) * page_block_size, D_QK, dtype)
     pool = pool.reshape(max(n_pages, 1), page_block_size, 1, D_QK)
     perm = np.random.default_rng(sperm).permutation(n_pages) if shuffle else np.arange(n_pages)
@@ -176,7 +185,7 @@ def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed:
     return MlaInputs(
         dtype=dtype, q_nope=q_nope, q_pe=q_pe, cache_seqlens=lens,
         softmax_scale=default_scale() if scale is None else float(scale),
-        pool=pool, block_table=table, page_block_size=page_block_size,
+        pool=pool, block_table=table, page_block_size=page_block_size, seqlen_q=seqlen_q,
         meta={"layout": "paged", "seed": seed, "n_pages": n_pages},
     )
 

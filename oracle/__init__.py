@@ -18,5 +18,6 @@ from .mla_oracle import (  # noqa: F401
     split_partial,
     split_ranges,
     to_f64,
+    visible_rows,
     weighted_values,
 )

@@ -34,9 +34,16 @@ variant speaks of blocks_per_split and remaining_blocks): the valid length is
 cut into 64-row blocks, split k of s gets floor(nb/s) blocks plus one more when
 k < nb mod s, in order.
 
+Several query tokens per sequence (speculative / multi-token decode): the
+FlashMLA analysis's parameter struct carries seqlen_q and is_causal.  Reading:
+the s = seqlen_q new tokens are the last s rows of the cache, and query token t
+(0-based, the newest last) sees rows j < L - (s - 1 - t); its H heads are query
+rows t*H .. t*H + H - 1 of the sequence (token-major).  s = 1 is plain decode.
+
 Readings where the pages are silent:
 * lse is returned in natural-log units (the kernel's base-2 value times ln 2).
-* L = 0 gives out = 0 and lse = -inf; an empty split contributes nothing.
+* L = 0 gives out = 0 and lse = -inf; an empty split contributes nothing.  A
+  negative L counts as 0.
 
 Every function here is fp64 NumPy; matrix products and exp/log are library
 primitives.  No blocking, fusion or reordering beyond what the definition and
@@ -130,24 +137,39 @@ def _layout_kwargs(inp) -> dict:
     return dict(kv_latent=inp.kv_latent, k_pe=inp.k_pe)
 
 
+def visible_rows(L: int, seqlen_q: int, t: int) -> int:
+    """Cache rows that query token t of seqlen_q sees in a sequence of L rows:
+    rows j < L - (seqlen_q - 1 - t), none when that is below 1."""
+    return max(0, max(int(L), 0) - (seqlen_q - 1 - t))
+
+
 def mla_decode_ref(inp, batches: Optional[Sequence[int]] = None,
                    heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Direct fp64 MLA decode of an ``MlaInputs``-like object.
 
     Returns ``out [nb, nh, 512]`` and ``lse [nb, nh]`` for the selected
-    sequences (default all) and heads (default all), in that order.
+    sequences (default all) and query rows (default all), in that order.  Query
+    row v belongs to token v // heads_per_token (``inp.seqlen_q`` tokens,
+    default 1), which sees the rows given by ``visible_rows``.
     """
+    sq = int(getattr(inp, "seqlen_q", 1))
+    hpt = inp.heads // sq
     bsel = list(range(inp.batch)) if batches is None else list(batches)
     hsel = np.arange(inp.heads) if heads is None else np.asarray(list(heads))
     out = np.zeros((len(bsel), len(hsel), D_LATENT))
     lse = np.zeros((len(bsel), len(hsel)))
     kw = _layout_kwargs(inp)
     for i, b in enumerate(bsel):
-        L = int(inp.cache_seqlens[b])
+        L = max(int(inp.cache_seqlens[b]), 0)
         K = cache_rows(b, L, inp.dtype, **kw)
-        qn = to_f64(inp.q_nope[b][hsel], inp.dtype)
-        qp = to_f64(inp.q_pe[b][hsel], inp.dtype)
-        out[i], lse[i] = attend(qn, qp, K, inp.softmax_scale)
+        for t in range(sq):
+            idx = np.nonzero(hsel // hpt == t)[0]
+            if idx.size == 0:
+                continue
+            rows = hsel[idx]
+            qn = to_f64(inp.q_nope[b][rows], inp.dtype)
+            qp = to_f64(inp.q_pe[b][rows], inp.dtype)
+            out[i, idx], lse[i, idx] = attend(qn, qp, K[:visible_rows(L, sq, t)], inp.softmax_scale)
     return out, lse
 
 
@@ -213,14 +235,22 @@ def mla_decode_split_ref(inp, splits, batches: Optional[Sequence[int]] = None,
     out = np.zeros((len(bsel), len(hsel), D_LATENT))
     lse = np.zeros((len(bsel), len(hsel)))
     kw = _layout_kwargs(inp)
+    sq = int(getattr(inp, "seqlen_q", 1))
+    hpt = inp.heads // sq
     for i, b in enumerate(bsel):
         s = splits if np.isscalar(splits) else splits[b]
-        L = int(inp.cache_seqlens[b])
+        L = max(int(inp.cache_seqlens[b]), 0)
         K = cache_rows(b, L, inp.dtype, **kw)
-        qn = to_f64(inp.q_nope[b][hsel], inp.dtype)
-        qp = to_f64(inp.q_pe[b][hsel], inp.dtype)
-        parts = [split_partial(qn, qp, K[r0:r1], inp.softmax_scale)
-                 for r0, r1 in split_ranges(L, int(s), block_rows)]
-        out[i], lse[i] = combine(parts)
+        for t in range(sq):
+            idx = np.nonzero(hsel // hpt == t)[0]
+            if idx.size == 0:
+                continue
+            rows = hsel[idx]
+            qn = to_f64(inp.q_nope[b][rows], inp.dtype)
+            qp = to_f64(inp.q_pe[b][rows], inp.dtype)
+            Lt = visible_rows(L, sq, t)
+            parts = [split_partial(qn, qp, K[r0:max(r0, min(r1, Lt))], inp.softmax_scale)
+                     for r0, r1 in split_ranges(L, int(s), block_rows)]
+            out[i, idx], lse[i, idx] = combine(parts)
     return out, lse
 

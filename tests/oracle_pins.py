@@ -229,6 +229,30 @@ def pin_split_ranges(orc):
             assert nblk == sorted(nblk, reverse=True) or L % 64 != 0
 
 
+def pin_multi_token(orc):
+    """Three query tokens per sequence: token t's rows (t*H .. t*H + H - 1) give
+    exactly plain one-token decode over the first L - (2 - t) cache rows
+    (lengths written out by hand below), in the direct and the split form."""
+    H = 4
+    lens = [40, 3, 1, 0]
+    inp = mi.make_contiguous(len(lens), H, 40, lens, "f16", seed=33, seqlen_q=3)
+    o3, l3 = orc.mla_decode_ref(inp)
+    visible = {0: [38, 1, 0, 0], 1: [39, 2, 0, 0], 2: [40, 3, 1, 0]}   # per token t, per sequence
+    for t, vis in visible.items():
+        one = mi.MlaInputs(dtype="f16", q_nope=inp.q_nope[:, t * H:(t + 1) * H].copy(),
+                           q_pe=inp.q_pe[:, t * H:(t + 1) * H].copy(),
+                           cache_seqlens=np.array(vis, np.int32), softmax_scale=inp.softmax_scale,
+                           kv_latent=inp.kv_latent, k_pe=inp.k_pe)
+        o1, l1 = orc.mla_decode_ref(one)
+        assert np.array_equal(o3[:, t * H:(t + 1) * H], o1), t
+        assert np.array_equal(l3[:, t * H:(t + 1) * H], l1), t
+    for s in (1, 2, 5):
+        os_, ls_ = orc.mla_decode_split_ref(inp, s)
+        _close(os_, o3, 1e-11, 1e-12, f"multi-token split {s} out")
+        both = np.isneginf(ls_) & np.isneginf(l3)
+        _close(np.where(both, 0, ls_), np.where(both, 0, l3), 1e-12, 1e-12, f"multi-token split {s} lse")
+
+
 def pin_batch_independence(orc):
     """Changing one sequence's cache leaves every other sequence bit-identical."""
     inp = mi.make_contiguous(3, 2, 50, [50, 20, 35], "f16", seed=29)
@@ -311,6 +335,7 @@ ALL_PINS = [
     pin_page_permutation,
     pin_split_invariance,
     pin_split_ranges,
+    pin_multi_token,
     pin_batch_independence,
     pin_bruteforce,
 ]

@@ -41,7 +41,8 @@ def assert_parity(out, lse, ref_out, ref_lse, what=""):
     excess = np.abs(out - ref_out) - (ATOL + RTOL * np.abs(ref_out))
     assert excess.max() <= 0, f"{what}: out off by {excess.max():.3e} beyond tolerance at {np.unravel_index(excess.argmax(), excess.shape)}"
     both_inf = np.isneginf(lse) & np.isneginf(ref_lse)
-    err = np.where(both_inf, 0.0, np.abs(lse - ref_lse))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(lse - ref_lse))
     assert not np.isnan(err).any() and err.max() <= LSE_TOL, f"{what}: lse err {np.nanmax(err):.3e}"
 
 

@@ -34,6 +34,9 @@ MUTANTS = {
     "partial_base": ("return o, lse / math.log(2.0)", "return o, lse"),
     "stabiliser_shift": ("np.exp(z - m[:, None]).sum(axis=1)", "np.exp(z - m[:, None] + 1.0).sum(axis=1)"),
     "weights_not_normalised": ("np.exp(z - lse[:, None]) @ V", "np.exp(z) @ V"),
+    "causal_direction": ("max(int(L), 0) - (seqlen_q - 1 - t)", "max(int(L), 0) - t"),
+    "causal_offset": ("max(int(L), 0) - (seqlen_q - 1 - t)", "max(int(L), 0) - (seqlen_q - t)"),
+    "token_major_rows": ("hsel // hpt == t", "hsel % sq == t"),
 }
 
 

@@ -66,8 +66,10 @@ def mla_num_cus(device: Optional[int] = None) -> int:
     return n.value
 
 
-def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out) -> MlaDesc:
-    """Fill an ``MlaDesc`` from tensors (strides in elements)."""
+def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q: int = 1) -> MlaDesc:
+    """Fill an ``MlaDesc`` from tensors (strides in elements).  With
+    ``seqlen_q`` > 1 the H query rows are seqlen_q tokens x H / seqlen_q heads,
+    token-major."""
     if q_nope.dim() != 3 or q_nope.shape[2] != D_LATENT or q_nope.stride(2) != 1:
         raise ValueError(f"q_nope must be [B, H, 512] with contiguous last dim, got {tuple(q_nope.shape)}")
     B, H = q_nope.shape[0], q_nope.shape[1]
@@ -81,6 +83,7 @@ def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out) -> MlaDesc:
         raise ValueError("kv_latent and k_pe disagree on [N, rows]")
     d = MlaDesc()
     d.batch, d.heads = B, H
+    d.seqlen_q = int(seqlen_q)
     d.d_latent, d.d_rope = D_LATENT, D_ROPE
     d.dtype = _dtype_code(q_nope)
     for t, nm in ((q_pe, "q_pe"), (kv, "kv_latent"), (kp, "k_pe"), (out, "out")):
@@ -138,10 +141,28 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     and ``block_table`` is int32 ``[B, max_blocks]``.  ``num_split=0`` lets the
     planner choose the splits.  Work is enqueued on ``stream`` (default: the
     current stream) and nothing synchronises.
+
+    Several query tokens per sequence: ``q_nope [B, s, H, 512]`` and ``q_pe
+    [B, s, H, 64]`` (the s new tokens are the last s cache rows; token t sees
+    rows j < L - (s - 1 - t)); then ``out`` is ``[B, s, H, 512]`` and ``lse``
+    ``[B, s, H]``.
     """
     torch = _torch()
     if not q_nope.is_cuda:
         raise ValueError("tensors must live on the GPU")
+    seqlen_q, four_d = 1, q_nope.dim() == 4
+    if four_d:
+        B, seqlen_q, Hq = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+        if q_pe.dim() != 4 or tuple(q_pe.shape[:3]) != (B, seqlen_q, Hq):
+            raise ValueError("q_pe must be [B, s, H, 64] like q_nope")
+        if out is None:
+            out = torch.empty((B, seqlen_q, Hq, D_LATENT), dtype=q_nope.dtype, device=q_nope.device)
+        if lse is None:
+            lse = torch.empty((B, seqlen_q, Hq), dtype=torch.float32, device=q_nope.device)
+        out4, lse4 = out, lse
+        # Query rows token-major: views only (the kernel writes through out/lse).
+        q_nope, q_pe, out, lse = (_rows_view(q_nope, "q_nope"), _rows_view(q_pe, "q_pe"), _rows_view(out, "out"),
+                                  _rows_view(lse, "lse"))
     B, H = q_nope.shape[0], q_nope.shape[1]
     if out is None:
         out = torch.empty((B, H, D_LATENT), dtype=q_nope.dtype, device=q_nope.device)
@@ -153,7 +174,7 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
         raise ValueError("cache_seqlens must be a contiguous int32 tensor")
     if block_table is not None and (block_table.dtype != torch.int32 or block_table.stride(1) != 1):
         raise ValueError("block_table must be int32 with contiguous rows")
-    desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out)
+    desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q)
     s = torch.cuda.current_stream(q_nope.device) if stream is None else stream
     if workspace is None:
         need = mla_workspace_size(desc, num_split, mla_num_cus(q_nope.device.index))
@@ -166,45 +187,54 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
         float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), s.cuda_stream)
     _lib.check(st)
+    if four_d:
+        return out4, lse4
     return out, lse
 
 
-def mla_plan_host(cache_seqlens, heads: int, num_split: int, num_cus: int):
-    """Host twin of the planner.  Returns (num_splits [B], split_offset [B+1], work [W, 4]) as numpy."""
+def _rows_view(t, name):
+    """[B, s, H, ...] -> [B, s*H, ...] as a view (token-major query rows)."""
+    if t.stride(1) != t.shape[2] * t.stride(2):
+        raise ValueError(f"{name}: the token and head dimensions must be mergeable into one (token-major rows)")
+    return t.view(t.shape[0], t.shape[1] * t.shape[2], *t.shape[3:])
+
+
+def _plan_capacity(batch: int, heads: int, num_split: int, num_cus: int, seqlen_q: int) -> int:
+    """Split entries a plan can need (the library's own count, via mla_max_work)."""
+    d = MlaDesc()
+    d.batch, d.heads, d.d_latent, d.d_rope, d.dtype, d.seqlen_q = int(batch), int(heads), 512, 64, 0, int(seqlen_q)
+    return mla_max_work(d, num_split, num_cus)
+
+
+def mla_plan_host(cache_seqlens, heads: int, num_split: int, num_cus: int, seqlen_q: int = 1):
+    """Host twin of the planner.  Returns (num_splits [B], split_offset [B+1], work [W, 4]) as numpy.
+    ``heads`` counts query rows (seqlen_q x heads per token)."""
     import numpy as np
     lens = np.ascontiguousarray(cache_seqlens, dtype=np.int32)
     B = lens.shape[0]
-    if num_split > 0:
-        max_work = B * num_split
-    else:
-        hg = -(-heads // 128)
-        max_work = max(B, -(-num_cus // hg))
+    max_work = _plan_capacity(B, heads, num_split, num_cus, seqlen_q)
     ns = np.zeros(B, np.int32)
     off = np.zeros(B + 1, np.int32)
     work = np.zeros((max(max_work, 1), 4), np.int32)
     _lib.check(_lib.lib().mla_plan_host(
-        lens.ctypes.data, B, int(heads), int(num_split), int(num_cus), ns.ctypes.data, off.ctypes.data,
-        work.ctypes.data, int(max_work)))
+        lens.ctypes.data, B, int(heads), int(seqlen_q), int(num_split), int(num_cus), ns.ctypes.data,
+        off.ctypes.data, work.ctypes.data, int(max_work)))
     return ns, off, work[:off[B]]
 
 
-def mla_plan_device(cache_seqlens, heads: int, num_split: int, num_cus: int, stream=None):
+def mla_plan_device(cache_seqlens, heads: int, num_split: int, num_cus: int, stream=None, seqlen_q: int = 1):
     """Device planner; returns (num_splits, split_offset, work) as torch tensors on the GPU."""
     torch = _torch()
     B = cache_seqlens.shape[0]
-    if num_split > 0:
-        max_work = B * num_split
-    else:
-        hg = -(-heads // 128)
-        max_work = max(B, -(-num_cus // hg))
+    max_work = _plan_capacity(B, heads, num_split, num_cus, seqlen_q)
     dev = cache_seqlens.device
     ns = torch.zeros(B, dtype=torch.int32, device=dev)
     off = torch.zeros(B + 1, dtype=torch.int32, device=dev)
     work = torch.zeros((max(max_work, 1), 4), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream(dev) if stream is None else stream
     _lib.check(_lib.lib().mla_plan_device(
-        cache_seqlens.data_ptr(), B, int(heads), int(num_split), int(num_cus), ns.data_ptr(), off.data_ptr(),
-        work.data_ptr(), int(max_work), s.cuda_stream))
+        cache_seqlens.data_ptr(), B, int(heads), int(seqlen_q), int(num_split), int(num_cus), ns.data_ptr(),
+        off.data_ptr(), work.data_ptr(), int(max_work), s.cuda_stream))
     return ns, off, work
 
 

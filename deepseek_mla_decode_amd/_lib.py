@@ -34,7 +34,7 @@ class MlaDesc(ctypes.Structure):
         ("page_block_size", ctypes.c_int32),
         ("block_table_stride", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int32),
         ("q_nope_sb", ctypes.c_int64), ("q_nope_sh", ctypes.c_int64),
         ("q_pe_sb", ctypes.c_int64), ("q_pe_sh", ctypes.c_int64),
         ("kv_sb", ctypes.c_int64), ("kv_sr", ctypes.c_int64),
@@ -60,8 +60,8 @@ SIGNATURES = {
     "mla_num_cus": (ctypes.c_int, [ctypes.c_int, _PI32]),
     "mla_max_work": (ctypes.c_int, [ctypes.POINTER(MlaDesc), _I32, _I32, _PI32]),
     "mla_workspace_size": (ctypes.c_int, [ctypes.POINTER(MlaDesc), _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
-    "mla_plan_host": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _I32]),
-    "mla_plan_device": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "mla_plan_host": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32]),
+    "mla_plan_device": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
                                   ctypes.POINTER(MlaDesc), _P, ctypes.c_size_t, _P]),
     "mla_last_error": (ctypes.c_char_p, []),

@@ -67,9 +67,16 @@ int check_desc(const mla_desc* d) {
                 d->d_rope);
   if (d->dtype != MLA_DTYPE_F16 && d->dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
-  if (d->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (d->seqlen_q < 0) return fail(MLA_ERR_INVALID_ARG, "seqlen_q %d < 0", d->seqlen_q);
+  if (d->seqlen_q > mla::kMaxSeqlenQ)
+    return fail(MLA_ERR_UNSUPPORTED, "seqlen_q %d above %d", d->seqlen_q, mla::kMaxSeqlenQ);
+  if (d->seqlen_q > 1 && d->heads % d->seqlen_q != 0)
+    return fail(MLA_ERR_INVALID_ARG, "heads %d (query rows) is not a multiple of seqlen_q %d", d->heads,
+                d->seqlen_q);
   return MLA_OK;
 }
+
+int32_t seqlen_q_of(const mla_desc* d) { return d->seqlen_q < 1 ? 1 : d->seqlen_q; }
 
 int check_num_split(int32_t num_split) {
   if (num_split < 0 || num_split > MLA_MAX_SPLITS)
@@ -79,7 +86,7 @@ int check_num_split(int32_t num_split) {
 
 int max_work_of(const mla_desc* d, int32_t num_split, int32_t num_cus, int32_t* out) {
   if (num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "num_cus %d < 1", num_cus);
-  int64_t w = num_split > 0 ? (int64_t)d->batch * num_split : (int64_t)mla::planner_cap(d->batch, d->heads, num_cus);
+  const int64_t w = mla::max_splits(d->batch, d->heads, num_split, num_cus, seqlen_q_of(d));
   if (w > (int64_t)INT32_MAX / 4) return fail(MLA_ERR_INVALID_ARG, "too many work items (%lld)", (long long)w);
   *out = (int32_t)w;
   return MLA_OK;
@@ -160,24 +167,28 @@ int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus,
   return ok();
 }
 
-int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
-                  int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t seqlen_q,
+                  int32_t num_split, int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
                   int32_t max_work) {
   int st;
   if (batch < 0 || heads < 1 || num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "bad batch/heads/num_cus");
+  if (seqlen_q < 0 || seqlen_q > mla::kMaxSeqlenQ) return fail(MLA_ERR_INVALID_ARG, "bad seqlen_q %d", seqlen_q);
+  if (seqlen_q < 1) seqlen_q = 1;
   if ((st = check_num_split(num_split)) != MLA_OK) return st;
   if (batch > 0 && (!cache_seqlens || !num_splits || !work)) return fail(MLA_ERR_INVALID_ARG, "NULL array");
   if (!split_offset) return fail(MLA_ERR_INVALID_ARG, "NULL split_offset");
   const int32_t cap_rows = INT32_MAX;
+  const int32_t tail = mla::tail_splits(seqlen_q);
+  // Blocks of each sequence's prefix (the rows every query token sees).
   std::vector<int32_t> nb(batch);
   int32_t mx = 0;
   for (int b = 0; b < batch; ++b) {
-    nb[b] = mla::num_blocks(mla::clamp_len(cache_seqlens[b], cap_rows));
+    nb[b] = mla::num_blocks(mla::prefix_len(mla::clamp_len(cache_seqlens[b], cap_rows), seqlen_q));
     mx = nb[b] > mx ? nb[b] : mx;
   }
   int32_t t = 1;
   if (num_split == 0) {
-    const int64_t cap = mla::planner_cap(batch, heads, num_cus);
+    const int64_t cap = mla::planner_cap(batch, heads, num_cus, seqlen_q);
     int32_t lo = 1, hi = mx > 1 ? mx : 1;
     while (lo < hi) {
       const int32_t mid = lo + (hi - lo) / 2;
@@ -187,19 +198,20 @@ int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, in
     }
     t = lo;
   }
+  auto prefix_splits = [&](int b) { return num_split > 0 ? num_split : mla::splits_for_budget(nb[b], t); };
   int64_t total = 0;
-  for (int b = 0; b < batch; ++b) total += num_split > 0 ? num_split : mla::splits_for_budget(nb[b], t);
+  for (int b = 0; b < batch; ++b) total += prefix_splits(b) + tail;
   if (total > max_work) return fail(MLA_ERR_INVALID_ARG, "plan needs %lld work items > max_work %d",
                                     (long long)total, max_work);
   int32_t off = 0;
   for (int b = 0; b < batch; ++b) {
     const int32_t L = mla::clamp_len(cache_seqlens[b], cap_rows);
-    const int32_t s = num_split > 0 ? num_split : mla::splits_for_budget(nb[b], t);
+    const int32_t sp = prefix_splits(b), s = sp + tail;
     num_splits[b] = s;
     split_offset[b] = off;
     for (int32_t k = 0; k < s; ++k) {
       int32_t r0, r1;
-      mla::split_range(L, s, k, &r0, &r1);
+      mla::seq_split_range(L, seqlen_q, sp, k, &r0, &r1);
       int32_t* w = work + 4 * (size_t)(off + k);
       w[0] = b;
       w[1] = k;
@@ -212,15 +224,17 @@ int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, in
   return ok();
 }
 
-int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
-                    int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t seqlen_q,
+                    int32_t num_split, int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
                     int32_t max_work, hipStream_t stream) {
   int st;
   if (batch < 0 || heads < 1 || num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "bad batch/heads/num_cus");
+  if (seqlen_q < 0 || seqlen_q > mla::kMaxSeqlenQ) return fail(MLA_ERR_INVALID_ARG, "bad seqlen_q %d", seqlen_q);
+  if (seqlen_q < 1) seqlen_q = 1;
   if ((st = check_num_split(num_split)) != MLA_OK) return st;
   if (batch > 0 && (!cache_seqlens || !num_splits || !work)) return fail(MLA_ERR_INVALID_ARG, "NULL array");
   if (!split_offset) return fail(MLA_ERR_INVALID_ARG, "NULL split_offset");
-  const int64_t need = num_split > 0 ? (int64_t)batch * num_split : mla::planner_cap(batch, heads, num_cus);
+  const int64_t need = mla::max_splits(batch, heads, num_split, num_cus, seqlen_q);
   if (need > max_work) return fail(MLA_ERR_INVALID_ARG, "max_work %d < %lld", max_work, (long long)need);
   mla::PlanParams p{};
   p.seqlens = cache_seqlens;
@@ -231,6 +245,7 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
   p.heads = heads;
   p.num_split = num_split;
   p.num_cus = num_cus;
+  p.seqlen_q = seqlen_q;
   p.row_cap = INT32_MAX;
   hipError_t e = mla::launch_plan(p, stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
@@ -322,7 +337,12 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.kpe_sr = d->kpe_sr;
   sp.out_sb = d->out_sb;
   sp.out_sh = d->out_sh;
-  sp.num_split = num_split;
+  // Forced mode: splits per sequence, the tail included.
+  const int32_t seqlen_q = seqlen_q_of(d);
+  const int32_t per_seq = num_split > 0 ? num_split + mla::tail_splits(seqlen_q) : 0;
+  sp.num_split = per_seq;
+  sp.seqlen_q = seqlen_q;
+  sp.heads_per_token = d->heads / seqlen_q;
   sp.batch = d->batch;
   sp.heads = d->heads;
   sp.page_size = paged ? d->page_block_size : 1;
@@ -343,7 +363,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "redo launch: %s", hipGetErrorString(e));
 
-  if (num_split != 1) {
+  if (per_seq != 1) {
     mla::CombineParams cp{};
     cp.part_o = part_o;
     cp.part_lse = part_lse;
@@ -352,10 +372,10 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     cp.lse = lse;
     cp.out_sb = d->out_sb;
     cp.out_sh = d->out_sh;
-    cp.num_split = num_split;
+    cp.num_split = per_seq;
     cp.heads = d->heads;
     // Splits per sequence on average: forced, or at most max_work / B.
-    const int mean_splits = num_split > 0 ? num_split : (max_work + d->batch - 1) / (d->batch > 0 ? d->batch : 1);
+    const int mean_splits = per_seq > 0 ? per_seq : (max_work + d->batch - 1) / (d->batch > 0 ? d->batch : 1);
     if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream, ev ? ev[4] : nullptr,
                                  ev ? ev[5] : nullptr)) != hipSuccess)
       return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));

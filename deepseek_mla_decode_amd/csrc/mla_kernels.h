@@ -26,7 +26,9 @@ struct SplitParams {
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
   int64_t out_sb, out_sh;
-  int32_t num_split;            // > 0 forced, 0 planner mode
+  int32_t num_split;            // > 0 forced splits per sequence (the tail included), 0 planner mode
+  int32_t seqlen_q;             // query tokens per sequence (>= 1)
+  int32_t heads_per_token;      // heads / seqlen_q
   int32_t batch, heads;
   int32_t page_size, bt_stride;
   int32_t num_pages;            // paged: page indices are clamped to [0, num_pages)
@@ -51,7 +53,7 @@ struct PlanParams {
   int32_t* num_splits;
   int32_t* split_offset;
   int32_t* work;
-  int32_t batch, heads, num_split, num_cus;
+  int32_t batch, heads, num_split, num_cus, seqlen_q;
   int32_t row_cap;              // lengths are clamped to [0, row_cap]
 };
 

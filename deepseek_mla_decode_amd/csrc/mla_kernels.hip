@@ -314,15 +314,19 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
     }
     return clamp_len(p.seqlens[b], p.row_cap);
   };
-  // Splits of the lane's sequences under budget t.
+  const int sq = p.seqlen_q, tail = tail_splits(sq);
+  // Blocks of the prefix of a sequence of L rows (the part the budget cuts).
+  auto pre_blocks = [&](int L) __attribute__((always_inline)) { return num_blocks(prefix_len(L, sq)); };
+  // Splits of the lane's sequences under budget t, tails included.
   auto lane_splits = [&](int t) __attribute__((always_inline)) -> int {
     int cnt = 0;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kPlanRegs; ++j)
-        if (j < per) cnt += Lr[j] >= 0 ? splits_for_budget(num_blocks(Lr[j]), t) : 0;
+        if (j < per) cnt += Lr[j] >= 0 ? splits_for_budget(pre_blocks(Lr[j]), t) + tail : 0;
     } else {
-      for (int b = b0; b < b1; ++b) cnt += splits_for_budget(num_blocks(clamp_len(p.seqlens[b], p.row_cap)), t);
+      for (int b = b0; b < b1; ++b)
+        cnt += splits_for_budget(pre_blocks(clamp_len(p.seqlens[b], p.row_cap)), t) + tail;
     }
     return cnt;
   };
@@ -332,13 +336,13 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
 #pragma unroll
     for (int j = 0; j < kPlanRegs; ++j)
       if (j < per) {
-        const int nb = Lr[j] >= 0 ? num_blocks(Lr[j]) : 0;
+        const int nb = Lr[j] >= 0 ? pre_blocks(Lr[j]) : 0;
         maxnb = max(maxnb, nb);
         sumnb += nb;
       }
   } else {
     for (int b = b0; b < b1; ++b) {
-      const int nb = num_blocks(clamp_len(p.seqlens[b], p.row_cap));
+      const int nb = pre_blocks(clamp_len(p.seqlens[b], p.row_cap));
       maxnb = max(maxnb, nb);
       sumnb += nb;
     }
@@ -347,7 +351,7 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   sumnb = wave_sum_i64(sumnb);
   // Smallest budget t with sum_b splits_for_budget(nb_b, t) <= cap; the sum
   // is at least sum_b nb_b / t, so t starts at ceil(sum nb / cap).
-  const int cap = planner_cap(B, p.heads, p.num_cus);
+  const int cap = planner_cap(B, p.heads, p.num_cus, sq);
   int hi = maxnb > 1 ? maxnb : 1;
   int64_t lo64 = (sumnb + cap - 1) / cap;
   int lo = (int)(lo64 < 1 ? 1 : (lo64 > hi ? hi : lo64));
@@ -364,12 +368,12 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
     int o = off;
     for (int b = b0; b < b1; ++b) {
       const int L = clamp_len(p.seqlens[b], p.row_cap);
-      const int sb = splits_for_budget(num_blocks(L), t);
+      const int spre = splits_for_budget(pre_blocks(L), t), sb = spre + tail;
       p.num_splits[b] = sb;
       p.split_offset[b] = o;
       for (int k = 0; k < sb; ++k) {
         int r0, r1;
-        split_range(L, sb, k, &r0, &r1);
+        seq_split_range(L, sq, spre, k, &r0, &r1);
         int* w = p.work + 4 * (o + k);
         w[0] = b;
         w[1] = k;
@@ -391,7 +395,7 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
     int o = off;
     for (int b = b0; b < b1; ++b) {
       const int L = len_of(b - b0, b);
-      const int sb = splits_for_budget(num_blocks(L), t);
+      const int sb = splits_for_budget(pre_blocks(L), t) + tail;
       if (wi < o + sb) {
         fb = b;
         fk = wi - o;
@@ -404,8 +408,9 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   it.b = __shfl(fb, owner);
   it.k = __shfl(fk, owner);
   const int L = __shfl(fL, owner);
-  it.s_b = splits_for_budget(num_blocks(L), t);
-  split_range(L, it.s_b, it.k, &it.r0, &it.r1);
+  const int spre = splits_for_budget(pre_blocks(L), t);
+  it.s_b = spre + tail;
+  seq_split_range(L, sq, spre, it.k, &it.r0, &it.r1);
   return it;
 }
 
@@ -611,7 +616,10 @@ struct Softmax {
     }
     if (s == 5) {
       mx = max3(mx, tmax, tmax);
-      if (!REDO && first) nmc = -(tmax * c);
+      // A query row with no visible row in the first tile (possible in a tail
+      // split) has tmax = -inf: it uses 0 as the max, so that P = 2^-inf = 0
+      // rather than 2^(-inf + inf).
+      if (!REDO && first) nmc = tmax == -__builtin_inff() ? 0.f : -(tmax * c);
     }
     if (s >= 6 && s < 22) {
       const int e = s - 6;
@@ -684,12 +692,14 @@ void split_kernel(SplitParams p) {
   if (REDO && *redo_flag == 0) return;
 
   // ---- work item (uniform) -------------------------------------------------
-  int b, r0, r1, s_b;
+  // k: the split's index within its sequence; with several query tokens the
+  // last split (k = s_b - 1) is the tail, whose rows are masked per query row.
+  int b, k, r0, r1, s_b;
   if (p.num_split > 0) {
     b = wi / p.num_split;
-    const int k = wi - b * p.num_split;
-    split_range(clamp_len(p.seqlens[b], p.row_cap), p.num_split, k, &r0, &r1);
+    k = wi - b * p.num_split;
     s_b = p.num_split;
+    seq_split_range(clamp_len(p.seqlens[b], p.row_cap), p.seqlen_q, s_b - tail_splits(p.seqlen_q), k, &r0, &r1);
   } else if (!REDO) {
     const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
     if (!it.valid) {   // past the end of the plan
@@ -697,16 +707,24 @@ void split_kernel(SplitParams p) {
       return;
     }
     b = it.b;
+    k = it.k;
     r0 = it.r0;
     r1 = it.r1;
     s_b = it.s_b;
   } else {
     // The plan the main pass published (the flag was set, so wi is in it).
     b = p.work[4 * wi + 0];
+    k = p.work[4 * wi + 1];
     r0 = p.work[4 * wi + 2];
     r1 = p.work[4 * wi + 3];
     s_b = p.split_offset[b + 1] - p.split_offset[b];
   }
+  // Tail splits (the last two with several query tokens): query token t sees
+  // rows j < L - (seqlen_q - 1 - t) = tail_lim + t.  Other splits: no limit.
+  int tail_lim = INT32_MAX;
+  if (p.seqlen_q > 1 && k >= s_b - tail_splits(p.seqlen_q))
+    tail_lim = clamp_len(p.seqlens[b], p.row_cap) - (p.seqlen_q - 1);
+  tail_lim = __builtin_amdgcn_readfirstlane(tail_lim);
   b = __builtin_amdgcn_readfirstlane(b);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
@@ -791,7 +809,11 @@ void split_kernel(SplitParams p) {
   for (int vb = 0; vb < 16; ++vb) acc[vb] = f32x16{};
   // Reference max m (raw-score units): the REDO launch reads it, the main
   // pass takes it from the first tile.
-  float nmc = REDO ? -(p.part_lse[(int64_t)wi * p.heads + h] * c) : 0.f;
+  float nmc = 0.f;
+  if (REDO) {
+    const float m = p.part_lse[(int64_t)wi * p.heads + h];
+    nmc = m == -__builtin_inff() ? 0.f : -(m * c);
+  }
   float mx = -__builtin_inff();   // running max of all tiles seen (raw)
   float lsum = 0.f;               // this lane's share of the sum of P
 
@@ -949,10 +971,14 @@ void split_kernel(SplitParams p) {
     nops_after_mfma(last);
     {
       const int tile_base = r0 + (n_tiles - 1) * kTileRows;
+      // This lane's row limit: r1, and in a tail split also the rows its
+      // query token t sees (tail_lim + t; tail_lim is INT32_MAX elsewhere).
+      const int tok = min(h0 + (lane_id() & 31), p.heads - 1) / p.heads_per_token;
+      const int lim = min(r1, tail_lim == INT32_MAX ? INT32_MAX : tail_lim + tok);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int n = 8 * (e >> 2) + 4 * (lane_id() >> 5) + (e & 3);
-        sm.x[e] = tile_base + n < r1 ? last[e] : -__builtin_inff();
+        sm.x[e] = tile_base + n < lim ? last[e] : -__builtin_inff();
       }
 #pragma unroll
       for (int s = 0; s < kSoftmaxSteps; ++s) sm.step(s, n_tiles == 1, c, nmc, mx, lsum);
@@ -1295,30 +1321,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 
   // Budget t: forced mode uses s_b = num_split; planner mode searches the
   // smallest t whose split total fits the cap.
+  const int sq = p.seqlen_q, tail = tail_splits(sq);
+  auto pre_blocks = [&](int b) { return num_blocks(prefix_len(clamp_len(p.seqlens[b], p.row_cap), sq)); };
   int t = 1;
   if (p.num_split == 0) {
     int mx = 0;
-    for (int b = tid; b < B; b += kPlanThreads) mx = max(mx, num_blocks(clamp_len(p.seqlens[b], p.row_cap)));
+    for (int b = tid; b < B; b += kPlanThreads) mx = max(mx, pre_blocks(b));
     mx = block_max(mx, red);
-    const int cap = planner_cap(B, p.heads, p.num_cus);
+    const int cap = planner_cap(B, p.heads, p.num_cus, sq);
     int lo = 1, hi = mx > 1 ? mx : 1;
     while (lo < hi) {
       const int mid = lo + (hi - lo) / 2;
       int cnt = 0;
-      for (int b = tid; b < B; b += kPlanThreads)
-        cnt += splits_for_budget(num_blocks(clamp_len(p.seqlens[b], p.row_cap)), mid);
+      for (int b = tid; b < B; b += kPlanThreads) cnt += splits_for_budget(pre_blocks(b), mid);
       cnt = block_sum(cnt, red);
       if (cnt <= cap) hi = mid; else lo = mid + 1;
     }
     t = lo;
   }
+  // Prefix splits of sequence b.
+  auto spre_of = [&](int b) { return p.num_split > 0 ? p.num_split : splits_for_budget(pre_blocks(b), t); };
 
   // Contiguous chunk of sequences per thread; exclusive scan of chunk totals.
   const int per = (B + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   int mine = 0;
-  for (int b = b0; b < b1; ++b)
-    mine += p.num_split > 0 ? p.num_split : splits_for_budget(num_blocks(clamp_len(p.seqlens[b], p.row_cap)), t);
+  for (int b = b0; b < b1; ++b) mine += spre_of(b) + tail;
   __syncthreads();
   scan[tid] = mine;
   __syncthreads();
@@ -1331,12 +1359,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   int off = scan[tid] - mine;
   for (int b = b0; b < b1; ++b) {
     const int L = clamp_len(p.seqlens[b], p.row_cap);
-    const int s = p.num_split > 0 ? p.num_split : splits_for_budget(num_blocks(L), t);
+    const int spre = spre_of(b), s = spre + tail;
     p.num_splits[b] = s;
     p.split_offset[b] = off;
     for (int k = 0; k < s; ++k) {
       int r0, r1;
-      split_range(L, s, k, &r0, &r1);
+      seq_split_range(L, sq, spre, k, &r0, &r1);
       int* w = p.work + 4 * (off + k);
       w[0] = b;
       w[1] = k;

@@ -39,6 +39,40 @@ MLA_HD void split_range(int32_t L, int32_t s, int32_t k, int32_t* r0, int32_t* r
   *r1 = (int32_t)(b < L ? b : L);
 }
 
+// Several query tokens (seqlen_q = s > 1).  Query token t sees rows
+// j < L - (s - 1 - t), so the last s - 1 rows are seen by some tokens only.
+// The prefix, cut by the planner's splits, ends at the last multiple of 32 at
+// or below L - (s - 1) (every token sees it; a 32-row boundary keeps every
+// tile inside one page); the rest, at most 31 + 15 rows, forms two tail
+// splits of one tile each (the second may be empty), the only tiles whose
+// rows the kernel masks per query row.
+constexpr int kMaxSeqlenQ = 16;
+constexpr int kTailAlign = 32;
+
+MLA_HD int32_t tail_splits(int32_t seqlen_q) { return seqlen_q > 1 ? 2 : 0; }
+
+MLA_HD int32_t prefix_len(int32_t L, int32_t seqlen_q) {
+  if (seqlen_q <= 1) return L;
+  const int32_t seen_by_all = L > seqlen_q - 1 ? L - (seqlen_q - 1) : 0;
+  return seen_by_all / kTailAlign * kTailAlign;
+}
+
+// Rows [*r0, *r1) of split k of a sequence of L rows with s_pre prefix splits
+// (splits s_pre and s_pre + 1, present when seqlen_q > 1, are the tails).
+MLA_HD void seq_split_range(int32_t L, int32_t seqlen_q, int32_t s_pre, int32_t k, int32_t* r0, int32_t* r1) {
+  const int32_t Lp = prefix_len(L, seqlen_q);
+  const int32_t mid = Lp + kTailAlign < L ? Lp + kTailAlign : L;
+  if (k < s_pre) {
+    split_range(Lp, s_pre, k, r0, r1);
+  } else if (k == s_pre) {
+    *r0 = Lp;
+    *r1 = mid;
+  } else {
+    *r0 = mid;
+    *r1 = L;
+  }
+}
+
 // Splits given to a sequence of nb blocks when each work item may take up to t blocks.
 MLA_HD int32_t splits_for_budget(int32_t nb, int32_t t) {
   int32_t s = nb <= 0 ? 1 : ceil_div(nb, t);
@@ -47,10 +81,18 @@ MLA_HD int32_t splits_for_budget(int32_t nb, int32_t t) {
 
 MLA_HD int32_t head_groups(int32_t heads) { return ceil_div(heads, kHeadsPerGroup); }
 
-// Most work items the planner may emit (planner mode).
-MLA_HD int32_t planner_cap(int32_t batch, int32_t heads, int32_t num_cus) {
-  const int32_t per_group = ceil_div(num_cus, head_groups(heads));
+// Most prefix splits the planner may emit (planner mode): one work item per
+// CU and head group in all, the tails included, but at least one per sequence.
+MLA_HD int32_t planner_cap(int32_t batch, int32_t heads, int32_t num_cus, int32_t seqlen_q) {
+  const int32_t per_group = ceil_div(num_cus, head_groups(heads)) - batch * tail_splits(seqlen_q);
   return batch > per_group ? batch : per_group;
+}
+
+// Most work items (splits, the tails included) of a plan.
+MLA_HD int64_t max_splits(int32_t batch, int32_t heads, int32_t num_split, int32_t num_cus, int32_t seqlen_q) {
+  const int64_t per_seq_extra = tail_splits(seqlen_q);
+  if (num_split > 0) return (int64_t)batch * (num_split + per_seq_extra);
+  return (int64_t)planner_cap(batch, heads, num_cus, seqlen_q) + (int64_t)batch * per_seq_extra;
 }
 
 }  // namespace mla

@@ -83,6 +83,15 @@ typedef enum mla_dtype {
  *   kv_sr = kpe_sr = 576.  page_block_size must be a positive multiple of 32.
  *   Only entries for j < cache_seqlens[b] are read; other entries may hold
  *   anything (e.g. -1).  Entries that are read must lie in [0, num_pages).
+ *
+ * Several query tokens per sequence (speculative / multi-token decode; the
+ * FlashMLA analysis's parameter struct carries seqlen_q and is_causal):
+ * seqlen_q = s > 1 (at most 16) gives each sequence s query tokens, and
+ * `heads` counts query ROWS, s x (heads per token), token-major: row
+ * v = t * (heads / s) + h is head h of token t, and q/out strides address
+ * rows.  The s new tokens are the last s rows of the cache: token t
+ * (0-based, the newest last) sees rows j < L - (s - 1 - t), none if that is
+ * below 1.  heads must be a multiple of s.  seqlen_q 0 or 1 is plain decode.
  */
 typedef struct mla_desc {
   int32_t batch;               /* B >= 0                                         */
@@ -94,7 +103,7 @@ typedef struct mla_desc {
   int32_t page_block_size;     /* paged: rows per page                           */
   int32_t block_table_stride;  /* paged: int32 entries per block_table row       */
   int32_t num_pages;           /* paged: pages in the pool (documents the bound) */
-  int32_t reserved;            /* must be 0                                      */
+  int32_t seqlen_q;            /* query tokens per sequence (0 or 1: one)        */
   int64_t q_nope_sb, q_nope_sh;  /* q_nope[b,h,:]  at q_nope + b*sb + h*sh       */
   int64_t q_pe_sb, q_pe_sh;      /* q_pe[b,h,:]    at q_pe + b*sb + h*sh         */
   int64_t kv_sb, kv_sr;          /* latent: batch (or page) stride, row stride   */
@@ -114,22 +123,31 @@ typedef struct mla_desc {
  * nb = ceil(L_b / 64) blocks of sequence b are dealt out in order, split k
  * getting floor(nb / s_b) blocks plus one more when k < nb mod s_b.
  *
+ * With seqlen_q = s > 1 the splits above cut only a prefix that every query
+ * token sees: rows [0, Lp) with Lp the largest multiple of 32 not above
+ * L - (s - 1) (0 if that is negative).  Two more splits, the tails, take rows
+ * [Lp, min(Lp + 32, L)) and [min(Lp + 32, L), L) (the second may be empty), so
+ * s_b = num_split + 2 in forced mode.
+ *
  * How s_b is chosen (num_split == 0, "planner" mode) is this library's own
  * rule, meant to fill the compute units: one work item per CU is the target,
  * so the planner finds the smallest per-item block budget t with
- *   sum_b max(1, ceil(nb_b / t)) <= max(B, ceil(num_cus / head_groups))
- * and sets s_b = max(1, ceil(nb_b / t)), capped at MLA_MAX_SPLITS.
- * head_groups = ceil(H / 128).  With num_split > 0 every s_b = num_split,
- * including splits that end up empty.
+ *   sum_b max(1, ceil(nb_b / t)) <= max(B, ceil(num_cus / head_groups) - tails)
+ * and sets s_b = max(1, ceil(nb_b / t)) (+2 for the tails), the prefix count
+ * capped at MLA_MAX_SPLITS.  head_groups = ceil(H / 128) with H the query
+ * rows; tails = 2B when seqlen_q > 1, else 0; nb_b counts the prefix's blocks.
+ * With num_split > 0 every s_b = num_split (+2 for the tails), including splits
+ * that end up empty.
  */
 
 /* Number of compute units of `device` (queried once, cached). */
 int mla_num_cus(int device, int32_t* num_cus_out /* host */);
 
 /*
- * Upper bound on the work items a plan can have for this description:
- *   num_split > 0 : B * num_split
- *   num_split == 0: max(B, ceil(num_cus / head_groups))
+ * Upper bound on the work items a plan can have for this description
+ * (tail = 2 when desc->seqlen_q > 1, else 0):
+ *   num_split > 0 : B * (num_split + tail)
+ *   num_split == 0: max(B, ceil(num_cus / head_groups) - B * tail) + B * tail
  */
 int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32_t* max_work_out /* host */);
 
@@ -143,22 +161,23 @@ int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus,
 
 /*
  * Host twin of the planner: same integers as the device planner.
+ *   heads          query rows (as desc->heads); seqlen_q as desc->seqlen_q
  *   cache_seqlens  host int32[batch]
  *   num_splits     host int32[batch]            (out)
  *   split_offset   host int32[batch + 1]        (out)
  *   work           host int32[4 * max_work]     (out)
  *   max_work       capacity of `work` in items; MLA_ERR_INVALID_ARG if too small.
  */
-int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
-                  int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t seqlen_q,
+                  int32_t num_split, int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
                   int32_t max_work);
 
 /*
  * Device planner: one workgroup reads cache_seqlens (device int32[batch]) and
  * writes num_splits / split_offset / work (device arrays as in mla_plan_host).
  */
-int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t num_split,
-                    int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
+int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t seqlen_q,
+                    int32_t num_split, int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
                     int32_t max_work, hipStream_t stream);
 
 /*

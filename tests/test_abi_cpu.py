@@ -66,7 +66,9 @@ def _decode(L, desc, num_split=0, scale=1 / 24, ptrs=None, block_table=None, ws=
     ("zero_heads", _lib.MLA_ERR_INVALID_ARG),
     ("dims", _lib.MLA_ERR_UNSUPPORTED),
     ("dtype", _lib.MLA_ERR_UNSUPPORTED),
-    ("reserved", _lib.MLA_ERR_INVALID_ARG),
+    ("neg_seqlen_q", _lib.MLA_ERR_INVALID_ARG),
+    ("big_seqlen_q", _lib.MLA_ERR_UNSUPPORTED),
+    ("heads_not_multiple_of_seqlen_q", _lib.MLA_ERR_INVALID_ARG),
     ("neg_split", _lib.MLA_ERR_INVALID_ARG),
     ("huge_split", _lib.MLA_ERR_INVALID_ARG),
     ("nan_scale", _lib.MLA_ERR_INVALID_ARG),
@@ -96,8 +98,12 @@ def test_validation_errors(L, case, expect):
         d.d_latent = 448
     elif case == "dtype":
         d.dtype = 7
-    elif case == "reserved":
-        d.reserved = 1
+    elif case == "neg_seqlen_q":
+        d.seqlen_q = -1
+    elif case == "big_seqlen_q":
+        d.seqlen_q = 17
+    elif case == "heads_not_multiple_of_seqlen_q":
+        d.seqlen_q = 3
     elif case == "neg_split":
         kw["num_split"] = -1
     elif case == "huge_split":
@@ -141,12 +147,15 @@ def test_empty_batch_is_ok_without_touching_memory(L):
 
 
 def test_workspace_size_formula(L):
-    for B, H, ns, cus in [(2, 16, 1, 256), (64, 128, 0, 256), (2, 128, 64, 256), (3, 200, 0, 256), (500, 128, 0, 256)]:
+    for B, H, ns, cus, sq in [(2, 16, 1, 256, 1), (64, 128, 0, 256, 1), (2, 128, 64, 256, 1), (3, 200, 0, 256, 1),
+                              (500, 128, 0, 256, 1), (64, 256, 0, 256, 2), (3, 96, 5, 256, 3), (200, 128, 0, 256, 4)]:
         d = _desc(B=B, H=H)
+        d.seqlen_q = sq
         w = ctypes.c_int32()
         assert L.mla_max_work(ctypes.byref(d), ns, cus, ctypes.byref(w)) == 0
         hg = -(-H // 128)
-        want_w = B * ns if ns else max(B, -(-cus // hg))
+        tail = 2 if sq > 1 else 0
+        want_w = B * (ns + tail) if ns else max(B, -(-cus // hg) - B * tail) + B * tail
         assert w.value == want_w
         n = ctypes.c_size_t()
         assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0
@@ -157,9 +166,9 @@ def test_workspace_size_formula(L):
         assert n.value == r(part_o + 2048 * want_w * H)
 
 
-def _plan(lens, heads, ns, cus):
+def _plan(lens, heads, ns, cus, sq=1):
     from deepseek_mla_decode_amd import mla_plan_host
-    return mla_plan_host(np.asarray(lens, np.int32), heads, ns, cus)
+    return mla_plan_host(np.asarray(lens, np.int32), heads, ns, cus, seqlen_q=sq)
 
 
 def _check_ranges_against_oracle(lens, ns_arr, off, work):
@@ -207,3 +216,42 @@ def test_planner_budget_is_minimal_on_random_lengths():
         if t > 1:
             assert sum(max(1, -(-int(n) // (t - 1))) for n in nb) > cap
         _check_ranges_against_oracle(lens, nsa, off, work)
+
+
+@pytest.mark.parametrize("lens,heads,ns,sq", [
+    ([4096] * 64, 256, 0, 2), ([1, 0, 2, 3, 65, 66, 300], 96, 0, 3), ([100, 5], 64, 4, 4), ([0, 0], 32, 2, 2),
+    ([131072] * 2, 512, 0, 4),
+])
+def test_host_planner_tail_splits(lens, heads, ns, sq):
+    """Several query tokens: the splits cut the prefix -- rows every token sees,
+    down to a multiple of 32 -- as the oracle's split_ranges does, and two
+    single-tile tail splits take the rest."""
+    nsa, off, work = _plan(lens, heads, ns, 256, sq)
+    assert int(off[-1]) == work.shape[0]
+    for b, L in enumerate(lens):
+        s = int(nsa[b])
+        if ns:
+            assert s == ns + 2
+        Lp = max(L - (sq - 1), 0) // 32 * 32
+        mid = min(Lp + 32, L)
+        assert L - Lp <= 32 + 31 and Lp <= max(L - (sq - 1), 0)
+        want = oracle.split_ranges(Lp, s - 2) + [(Lp, mid), (mid, L)]
+        got = [(int(work[off[b] + k, 2]), int(work[off[b] + k, 3])) for k in range(s)]
+        assert got == want, (b, L, got, want)
+
+
+def test_split_starts_keep_tiles_inside_pages():
+    """Every nonempty split starts at a multiple of 32 rows, for any lengths,
+    query-token counts and split modes: a 32-row tile then never crosses a
+    page (page sizes are multiples of 32), which the paged tile loads rely
+    on."""
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        B = int(rng.integers(1, 120))
+        lens = rng.integers(0, 9000, size=B).astype(np.int32)
+        sq = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        heads = sq * int(rng.choice([16, 32, 64, 128]))
+        ns = int(rng.choice([0, 0, 1, 3, 7]))
+        nsa, off, work = _plan(lens, heads, ns, int(rng.choice([80, 256, 304])), sq)
+        nonempty = work[:, 3] > work[:, 2]
+        assert (work[nonempty, 2] % 32 == 0).all(), (sq, ns, work[nonempty][work[nonempty, 2] % 32 != 0][:3])

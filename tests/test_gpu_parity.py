@@ -202,11 +202,12 @@ def test_strided_tensors(mla):
 def test_device_planner_matches_host_twin(mla):
     import torch
     rng = np.random.default_rng(9)
-    for B, heads, ns, cus in [(64, 128, 0, 256), (3, 16, 0, 256), (200, 128, 0, 304), (7, 256, 0, 256),
-                              (5, 128, 6, 256), (1500, 128, 0, 256), (2, 128, 0, 256)]:
+    for B, heads, ns, cus, sq in [(64, 128, 0, 256, 1), (3, 16, 0, 256, 1), (200, 128, 0, 304, 1), (7, 256, 0, 256, 1),
+                                  (5, 128, 6, 256, 1), (1500, 128, 0, 256, 1), (2, 128, 0, 256, 1),
+                                  (64, 256, 0, 256, 2), (9, 96, 4, 256, 3), (300, 128, 0, 256, 4)]:
         lens = rng.integers(0, 40000, size=B).astype(np.int32)
-        hn, ho, hw = mla.mla_plan_host(lens, heads, ns, cus)
-        dn, do, dw = mla.mla_plan_device(torch.from_numpy(lens).cuda(), heads, ns, cus)
+        hn, ho, hw = mla.mla_plan_host(lens, heads, ns, cus, seqlen_q=sq)
+        dn, do, dw = mla.mla_plan_device(torch.from_numpy(lens).cuda(), heads, ns, cus, seqlen_q=sq)
         torch.cuda.synchronize()
         assert np.array_equal(hn, dn.cpu().numpy()) and np.array_equal(ho, do.cpu().numpy())
         W = int(ho[-1])
@@ -466,6 +467,72 @@ def test_max_forced_splits(mla):
     out, lse = _run(mla, inp, 1024)
     ro, rl = oracle.mla_decode_ref(inp)
     assert_parity(out, lse, ro, rl, "1024 forced splits")
+
+
+def _run_tokens(mla, inp, num_split):
+    """Decode with [B, s, H, *] queries (the binding's several-token form)."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    d = to_device(inp, "cuda")
+    B, s = inp.batch, inp.seqlen_q
+    H = inp.heads // s
+    qn = d["q_nope"].view(B, s, H, 512)
+    qp = d["q_pe"].view(B, s, H, 64)
+    out, lse = mla.mla_decode(qn, qp, d["kv_latent"], d["k_pe"], d["block_table"], d["cache_seqlens"],
+                              inp.softmax_scale, num_split=num_split)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (B, s, H, 512) and tuple(lse.shape) == (B, s, H)
+    return from_device(out).reshape(B, s * H, 512), from_device(lse).reshape(B, s * H)
+
+
+@pytest.mark.parametrize("dtype,paged,seqlen_q,heads", [
+    ("f16", False, 2, 128), ("bf16", True, 2, 128), ("f16", True, 4, 32), ("bf16", False, 3, 64),
+    ("f16", False, 16, 16),
+])
+@pytest.mark.parametrize("num_split", [0, 1, 3])
+def test_several_query_tokens(mla, dtype, paged, seqlen_q, heads, num_split):
+    """seqlen_q query tokens per sequence, token t seeing rows j < L - (s-1-t):
+    lengths below s - 1 (no rows for the first tokens), around tile and block
+    edges, and long; the last s - 1 rows form the tail split, masked per query
+    row.  192 query rows (3 x 64) leave the second head group half empty."""
+    lens = [0, 1, 2, 3, 15, 33, 64, 65, 300, 1000]
+    if paged:
+        inp = mi.make_paged(len(lens), heads, lens, dtype, seed=140, page_block_size=64, seqlen_q=seqlen_q)
+    else:
+        inp = mi.make_contiguous(len(lens), heads, 1000, lens, dtype, seed=140, seqlen_q=seqlen_q)
+    out, lse = _run_tokens(mla, inp, num_split)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"{seqlen_q} tokens {dtype} paged={paged} split={num_split}")
+
+
+def test_several_query_tokens_plan_is_published(mla):
+    """Planner mode with 2 query tokens: the plan the split kernel writes into
+    the workspace (prefix splits + one tail split per sequence) equals the host
+    twin's integers."""
+    import torch
+    from mla_inputs.torch_io import to_device
+    rng = np.random.default_rng(141)
+    B, sq, H = 80, 2, 128
+    lens = rng.integers(0, 3000, size=B).astype(np.int32)
+    inp = mi.make_contiguous(B, H, 3000, lens, "f16", seed=142, seqlen_q=sq)
+    d = to_device(inp, "cuda")
+    cus = mla.mla_num_cus(0)
+    hn, ho, hw = mla.mla_plan_host(lens, sq * H, 0, cus, seqlen_q=sq)
+    out = torch.empty((B, sq * H, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, sq * H), dtype=torch.float32, device="cuda")
+    desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, out, seqlen_q=sq)
+    ws = torch.empty(mla.mla_workspace_size(desc, 0, cus), dtype=torch.uint8, device="cuda")
+    mla.mla_decode(d["q_nope"].view(B, sq, H, 512), d["q_pe"].view(B, sq, H, 64), d["kv_latent"], d["k_pe"], None,
+                   d["cache_seqlens"], inp.softmax_scale, num_split=0, out=out.view(B, sq, H, 512),
+                   lse=lse.view(B, sq, H), workspace=ws)
+    torch.cuda.synchronize()
+    plan = ws[: 4 * (B + B + 1 + 4 * int(ho[-1]))].view(torch.int32).cpu().numpy()
+    assert np.array_equal(plan[:B], hn) and np.array_equal(plan[B:2 * B + 1], ho)
+    assert np.array_equal(plan[2 * B + 1:].reshape(-1, 4), hw.reshape(-1, 4)[: int(ho[-1])])
+    from mla_inputs.torch_io import from_device
+    b = int(np.argmax(lens))
+    ro, rl = oracle.mla_decode_ref(inp, batches=[b])
+    assert_parity(from_device(out)[b:b + 1], from_device(lse)[b:b + 1], ro, rl, "2 tokens, planner")
 
 
 def test_negative_lengths_count_as_zero(mla):

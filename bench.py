@@ -33,12 +33,18 @@ D_QK, D_V = 576, 512
 METRIC = "MLA decode TFLOPS + KV GB/s (% roofline), B=64/128 h=128 d=576/512"
 
 
-def workload_figures(lens, heads: int):
-    """Algorithmic flops and bytes of one call (cache rows, Q, out, lse)."""
+def workload_figures(lens, heads: int, seqlen_q: int = 1):
+    """Algorithmic flops and bytes of one call (cache rows, Q, out, lse).
+
+    `heads` counts query rows (seqlen_q tokens x heads per token); with several
+    query tokens, token t of s is charged only the L - (s - 1 - t) rows it
+    sees."""
     import numpy as np
-    rows = float(np.sum(np.asarray(lens, dtype=np.int64)))
-    B = len(lens)
-    flops = 2.0 * heads * (D_QK + D_V) * rows
+    L = np.maximum(np.asarray(lens, dtype=np.int64), 0)
+    rows = float(np.sum(L))
+    B, s = len(lens), seqlen_q
+    seen = float(sum(np.sum(np.maximum(L - (s - 1 - t), 0)) for t in range(s)))
+    flops = 2.0 * (heads // s) * (D_QK + D_V) * seen
     kv_bytes = rows * D_QK * 2
     total_bytes = kv_bytes + B * heads * (D_QK * 2 + D_V * 2 + 4)
     return flops, kv_bytes, total_bytes
@@ -76,9 +82,9 @@ def cpu_baseline(inp, budget_s: float):
         oracle.mla_decode_ref(inp, batches=[done])
         done += 1
     el = time.perf_counter() - t0
-    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads)
+    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads, inp.seqlen_q)
     return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} heads), fp64 NumPy, "
+            "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} query rows), fp64 NumPy, "
                       f"{el:.1f} s wall"}
 
 
@@ -94,6 +100,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
+    ap.add_argument("--seqlen-q", type=int, default=1,
+                    help="query tokens per sequence (speculative / multi-token decode), each of H heads")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,10 +117,10 @@ def main() -> int:
     from mla_inputs.torch_io import to_device
 
     t_gen = time.perf_counter()
-    inp = mi.make_config(args.config)
+    inp = mi.make_config(args.config, seqlen_q=args.seqlen_q)
     gen_s = time.perf_counter() - t_gen
     dev = to_device(inp, "cuda")
-    flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads)
+    flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads, inp.seqlen_q)
     # Rotate copies of the cache when one copy would fit in the 256 MiB last-level cache.
     copies = args.copies or (1 if kv_bytes > 1.5 * 2**30 else 3)
     devs = [dev]
@@ -125,18 +133,22 @@ def main() -> int:
             d2.update(kv_latent=dev["kv_latent"].clone(), k_pe=dev["k_pe"].clone())
         d2["q_nope"], d2["q_pe"] = dev["q_nope"].clone(), dev["q_pe"].clone()
         devs.append(d2)
-    B, H = inp.batch, inp.heads
+    B, H, S = inp.batch, inp.heads, inp.seqlen_q   # H: query rows (S tokens x H / S heads)
     outs = [torch.empty((B, H, 512), dtype=dev["q_nope"].dtype, device="cuda") for _ in devs]
     lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in devs]
-    desc = mla.make_desc(dev["q_nope"], dev["q_pe"], dev["kv_latent"], dev["k_pe"], dev["block_table"], outs[0])
+    desc = mla.make_desc(dev["q_nope"], dev["q_pe"], dev["kv_latent"], dev["k_pe"], dev["block_table"], outs[0],
+                         seqlen_q=S)
     ws = torch.empty(mla.mla_workspace_size(desc, args.num_split, mla.mla_num_cus()), dtype=torch.uint8,
                      device="cuda")
 
+    def tokens(t):   # query rows [B, H, ...] -> [B, S, H / S, ...] when S > 1
+        return t if S == 1 else t.view(B, S, H // S, *t.shape[2:])
+
     def step(i):
         d = devs[i % len(devs)]
-        mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], d["cache_seqlens"],
-                       inp.softmax_scale, num_split=args.num_split, out=outs[i % len(devs)],
-                       lse=lses[i % len(devs)], workspace=ws)
+        mla.mla_decode(tokens(d["q_nope"]), tokens(d["q_pe"]), d["kv_latent"], d["k_pe"],
+                       d["block_table"], d["cache_seqlens"], inp.softmax_scale, num_split=args.num_split,
+                       out=tokens(outs[i % len(devs)]), lse=tokens(lses[i % len(devs)]), workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -175,6 +187,7 @@ def main() -> int:
 
     cpu = cpu_baseline(inp, args.cpu_budget) if args.cpu_budget > 0 else None
 
+    workload = mi.CONFIG_NAMES[args.config] + (f"_q{S}" if S > 1 else "")
     tflops = flops / (ms * 1e-3) / 1e12
     ai = flops / total_bytes
     roof_tflops = min(HBM_PEAK_GBS * 1e9 * ai / 1e12, MFMA_PEAK_TFLOPS)
@@ -193,7 +206,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": inp.dtype,
         "data": "synthetic (seeded N(0,1), no dataset)",
-        "config": {"workload": mi.CONFIG_NAMES[args.config], "batch": B, "heads": H,
+        "config": {"workload": workload, "batch": B, "heads": H // S, "seqlen_q": S,
                    "seqlen_kv_mean": mean_L, "layout": "paged" if inp.paged else "contiguous",
                    "num_split": args.num_split or "planner", "input_copies": len(devs)},
         "us_per_call": round(ms * 1e3, 2),
@@ -205,7 +218,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": None if split_gbs is None else round(split_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": None if split_gbs is None else round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(mi.CONFIG_NAMES[args.config]), "kernel": "split_kernel"},
+                     "traffic": measured_traffic(workload), "kernel": "split_kernel"},
         # The same launch against the dense fp16/bf16 MFMA peak (its other bound).
         "mfma": {"achieved": None if split_avg <= 0 else round(flops / (split_avg * 1e-3) / 1e12, 1),
                  "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",

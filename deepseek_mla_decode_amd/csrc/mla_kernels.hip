@@ -317,16 +317,16 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   const int sq = p.seqlen_q, tail = tail_splits(sq);
   // Blocks of the prefix of a sequence of L rows (the part the budget cuts).
   auto pre_blocks = [&](int L) __attribute__((always_inline)) { return num_blocks(prefix_len(L, sq)); };
-  // Splits of the lane's sequences under budget t, tails included.
+  // Prefix splits of the lane's sequences under budget t (the budget bounds
+  // these; the tails come on top).
   auto lane_splits = [&](int t) __attribute__((always_inline)) -> int {
     int cnt = 0;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kPlanRegs; ++j)
-        if (j < per) cnt += Lr[j] >= 0 ? splits_for_budget(pre_blocks(Lr[j]), t) + tail : 0;
+        if (j < per) cnt += Lr[j] >= 0 ? splits_for_budget(pre_blocks(Lr[j]), t) : 0;
     } else {
-      for (int b = b0; b < b1; ++b)
-        cnt += splits_for_budget(pre_blocks(clamp_len(p.seqlens[b], p.row_cap)), t) + tail;
+      for (int b = b0; b < b1; ++b) cnt += splits_for_budget(pre_blocks(clamp_len(p.seqlens[b], p.row_cap)), t);
     }
     return cnt;
   };
@@ -361,7 +361,7 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
     else lo = mid + 1;
   }
   const int t = lo;
-  const int mine = lane_splits(t);
+  const int mine = lane_splits(t) + tail * (b1 - b0);   // all splits of the lane's sequences
   const int off = wave_excl_scan(mine, lane);
   const int total = __shfl(off + mine, 63);
   if (publish) {

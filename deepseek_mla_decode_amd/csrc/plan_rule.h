@@ -82,9 +82,11 @@ MLA_HD int32_t splits_for_budget(int32_t nb, int32_t t) {
 MLA_HD int32_t head_groups(int32_t heads) { return ceil_div(heads, kHeadsPerGroup); }
 
 // Most prefix splits the planner may emit (planner mode): one work item per
-// CU and head group in all, the tails included, but at least one per sequence.
+// CU and head group, at least one per sequence.  The tail splits (one tile
+// each) come on top: they take a CU only briefly.
 MLA_HD int32_t planner_cap(int32_t batch, int32_t heads, int32_t num_cus, int32_t seqlen_q) {
-  const int32_t per_group = ceil_div(num_cus, head_groups(heads)) - batch * tail_splits(seqlen_q);
+  (void)seqlen_q;
+  const int32_t per_group = ceil_div(num_cus, head_groups(heads));
   return batch > per_group ? batch : per_group;
 }
 

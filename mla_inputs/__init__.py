@@ -239,8 +239,9 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(idx: int, batch_subset: Optional[int] = None) -> MlaInputs:
-    """Build workload ``idx`` (0..4).  ``batch_subset`` keeps only the first sequences.
+def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1) -> MlaInputs:
+    """Build workload ``idx`` (0..4).  ``batch_subset`` keeps only the first sequences;
+    ``seqlen_q`` > 1 gives every sequence that many query tokens (of H heads each).
 
     0: B=2, H=16, L=256, fp16, contiguous.
     1: B=64, H=128, L=4096, fp16, contiguous.
@@ -260,14 +261,14 @@ def make_config(idx: int, batch_subset: Optional[int] = None) -> MlaInputs:
         if batch_subset is not None:
             lens = lens[:batch_subset]
             B = batch_subset
-        inp = make_paged(B, H, lens, "bf16", seed=3, page_block_size=64, max_blocks=256)
+        inp = make_paged(B, H, lens, "bf16", seed=3, page_block_size=64, max_blocks=256, seqlen_q=seqlen_q)
         inp.meta["config"] = CONFIG_NAMES[3]
         return inp
     elif idx == 4:
         B, H, L = 2, 128, 131072
         if batch_subset is not None:
             B = batch_subset
-        inp = make_paged(B, H, [L] * B, "bf16", seed=4, page_block_size=64, max_blocks=L // 64)
+        inp = make_paged(B, H, [L] * B, "bf16", seed=4, page_block_size=64, max_blocks=L // 64, seqlen_q=seqlen_q)
         inp.meta["scaled_rows"] = scale_random_rows(inp, 0.01, 8.0, seed=40)
         inp.meta["config"] = CONFIG_NAMES[4]
         return inp
@@ -275,6 +276,6 @@ def make_config(idx: int, batch_subset: Optional[int] = None) -> MlaInputs:
         raise ValueError(idx)
     if batch_subset is not None:
         B = batch_subset
-    inp = make_contiguous(B, H, L, [L] * B, dt, seed=idx)
+    inp = make_contiguous(B, H, L, [L] * B, dt, seed=idx, seqlen_q=seqlen_q)
     inp.meta["config"] = CONFIG_NAMES[idx]
     return inp

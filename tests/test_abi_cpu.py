@@ -155,7 +155,7 @@ def test_workspace_size_formula(L):
         assert L.mla_max_work(ctypes.byref(d), ns, cus, ctypes.byref(w)) == 0
         hg = -(-H // 128)
         tail = 2 if sq > 1 else 0
-        want_w = B * (ns + tail) if ns else max(B, -(-cus // hg) - B * tail) + B * tail
+        want_w = B * (ns + tail) if ns else max(B, -(-cus // hg)) + B * tail
         assert w.value == want_w
         n = ctypes.c_size_t()
         assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0

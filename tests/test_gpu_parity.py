@@ -535,6 +535,33 @@ def test_several_query_tokens_plan_is_published(mla):
     assert_parity(from_device(out)[b:b + 1], from_device(lse)[b:b + 1], ro, rl, "2 tokens, planner")
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(mla, case):
+    """Seeded random problems over the whole input space: batch, heads per
+    token, lengths (with zeros), query tokens, layout and page size, dtype and
+    split mode.  Every sequence is checked."""
+    rng = np.random.default_rng(1000 + case)
+    B = int(rng.integers(1, 40))
+    sq = int(rng.choice([1, 1, 1, 2, 3, 5]))
+    heads = int(rng.choice([1, 8, 16, 32, 64, 96, 128]))
+    if sq * heads > 512:
+        heads = 512 // sq
+    lens = rng.integers(0, 2500, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    dtype = str(rng.choice(["f16", "bf16"]))
+    ns = int(rng.choice([0, 0, 1, 2, 5, 17]))
+    if rng.random() < 0.5:
+        page = int(rng.choice([32, 64, 128, 256]))
+        inp = mi.make_paged(B, heads, lens, dtype, seed=2000 + case, page_block_size=page, seqlen_q=sq,
+                            spare_pages=int(rng.integers(0, 3)))
+    else:
+        inp = mi.make_contiguous(B, heads, int(lens.max()) + int(rng.integers(0, 40)), lens, dtype,
+                                 seed=2000 + case, seqlen_q=sq)
+    out, lse = _run_tokens(mla, inp, ns) if sq > 1 else _run(mla, inp, ns)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"random case {case}: B={B} s={sq} H={heads} {dtype} paged={inp.paged} ns={ns}")
+
+
 def test_negative_lengths_count_as_zero(mla):
     """cache_seqlens are device data, so the kernels clamp them instead of
     rejecting them: a negative length behaves as 0 (out 0, lse -inf), in

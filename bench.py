@@ -100,6 +100,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="query heads per token instead of the workload's (e.g. one tensor-parallel shard)")
     ap.add_argument("--seqlen-q", type=int, default=1,
                     help="query tokens per sequence (speculative / multi-token decode), each of H heads")
     args = ap.parse_args()
@@ -117,7 +119,7 @@ def main() -> int:
     from mla_inputs.torch_io import to_device
 
     t_gen = time.perf_counter()
-    inp = mi.make_config(args.config, seqlen_q=args.seqlen_q)
+    inp = mi.make_config(args.config, seqlen_q=args.seqlen_q, heads=args.heads or None)
     gen_s = time.perf_counter() - t_gen
     dev = to_device(inp, "cuda")
     flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads, inp.seqlen_q)
@@ -187,7 +189,8 @@ def main() -> int:
 
     cpu = cpu_baseline(inp, args.cpu_budget) if args.cpu_budget > 0 else None
 
-    workload = mi.CONFIG_NAMES[args.config] + (f"_q{S}" if S > 1 else "")
+    workload = (mi.CONFIG_NAMES[args.config] + (f"_q{S}" if S > 1 else "")
+                + (f"_heads{H // S}" if args.heads else ""))
     tflops = flops / (ms * 1e-3) / 1e12
     ai = flops / total_bytes
     roof_tflops = min(HBM_PEAK_GBS * 1e9 * ai / 1e12, MFMA_PEAK_TFLOPS)

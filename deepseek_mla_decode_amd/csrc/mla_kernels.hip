@@ -804,6 +804,46 @@ void split_kernel(SplitParams p) {
     return;
   }
 
+  // A wave whose 32 heads all lie past the last head (few heads per group)
+  // computes nothing: it only issues its share of every tile's loads and
+  // passes the same barriers as the other waves (prologue; one per step; the
+  // two around the overflow words), then leaves.  Wave 0 always has heads.
+  if (h0 >= p.heads) {
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      const int pg = PAGED ? cursor_page(cur) : 0;
+      const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(kk));
+#pragma unroll
+      for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+      cursor_next<PAGED>(cur, r1);
+    }
+    wait_cnt<2 * kLoadsPerTile, 15>();
+    barrier();
+    int pg_next = 0;
+    if (n_tiles > 1) {
+      if constexpr (PAGED) pg_next = cursor_page(cur);
+      wait_cnt<kLoadsPerTile, 0>();
+      barrier();
+    }
+    for (int t = 1; t < n_tiles; ++t) {
+      const DmaTile d = cursor_tile<PAGED>(cur, pg_next, r1, slot(t + 2));
+      cursor_next<PAGED>(cur, r1);
+#pragma unroll
+      for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+      if constexpr (PAGED) pg_next = cursor_page(cur);
+      wait_cnt<kLoadsPerTile, 0>();
+      barrier();
+    }
+    wait_cnt<0, 15>();
+    if (!REDO) {
+      int* flags = reinterpret_cast<int*>(lds_raw);
+      __syncthreads();
+      if (lane == 0) flags[wave] = 0;
+      __syncthreads();
+    }
+    return;
+  }
+
   f32x16 acc[16];
 #pragma unroll
   for (int vb = 0; vb < 16; ++vb) acc[vb] = f32x16{};

@@ -239,9 +239,11 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1) -> MlaInputs:
+def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1,
+                heads: Optional[int] = None) -> MlaInputs:
     """Build workload ``idx`` (0..4).  ``batch_subset`` keeps only the first sequences;
-    ``seqlen_q`` > 1 gives every sequence that many query tokens (of H heads each).
+    ``seqlen_q`` > 1 gives every sequence that many query tokens (of H heads each);
+    ``heads`` replaces H (e.g. one tensor-parallel shard's heads).
 
     0: B=2, H=16, L=256, fp16, contiguous.
     1: B=64, H=128, L=4096, fp16, contiguous.
@@ -249,6 +251,7 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1)
     3: B=64, H=128, L_b ~ U{1..16384}, bf16, paged (64), shuffled block_table.
     4: B=2, H=128, L=131072, bf16, paged (64), shuffled, 1% of rows x8.
     """
+    Hx = heads
     if idx == 0:
         B, H, L, dt = 2, 16, 256, "f16"
     elif idx == 1:
@@ -256,7 +259,7 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1)
     elif idx == 2:
         B, H, L, dt = 128, 128, 8192, "f16"
     elif idx == 3:
-        B, H = 64, 128
+        B, H = 64, Hx or 128
         lens = np.random.default_rng(np.random.SeedSequence([3, 1])).integers(1, 16384, size=B, endpoint=True)
         if batch_subset is not None:
             lens = lens[:batch_subset]
@@ -265,7 +268,7 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1)
         inp.meta["config"] = CONFIG_NAMES[3]
         return inp
     elif idx == 4:
-        B, H, L = 2, 128, 131072
+        B, H, L = 2, Hx or 128, 131072
         if batch_subset is not None:
             B = batch_subset
         inp = make_paged(B, H, [L] * B, "bf16", seed=4, page_block_size=64, max_blocks=L // 64, seqlen_q=seqlen_q)
@@ -276,6 +279,7 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1)
         raise ValueError(idx)
     if batch_subset is not None:
         B = batch_subset
+    H = Hx or H
     inp = make_contiguous(B, H, L, [L] * B, dt, seed=idx, seqlen_q=seqlen_q)
     inp.meta["config"] = CONFIG_NAMES[idx]
     return inp

@@ -284,6 +284,7 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
 
 struct WorkItem {
   int b, k, r0, r1, s_b;
+  int slot;     // split slot (sequence-major: split_offset[b] + k)
   bool valid;   // false: past the last work item of the plan
 };
 
@@ -387,26 +388,41 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   WorkItem it{};
   it.valid = wi < total;
   if (!it.valid) return it;
-  // The lane whose chunk holds work item wi finds its sequence and split.
-  const uint64_t owner_mask = __ballot(wi >= off && wi < off + mine);
-  const int owner = __builtin_ctzll(owner_mask);
-  int fb = 0, fk = 0, fL = 0;
+  // Work-item order (not slot order): with several query tokens the 2B tail
+  // splits first (item wi < 2B: sequence wi / 2, tail wi % 2), then the
+  // prefix splits in sequence order; the split kernel deals the two kinds to
+  // the XCDs separately.  Split slots stay sequence-major.
+  const int ntail = tail * B;
+  int owner, j = 0;
+  if (wi < ntail) {
+    owner = (wi / tail) / per;   // the lane holding sequence wi / tail
+  } else {
+    j = wi - ntail;              // the j-th prefix split
+    const int mine_pre = mine - tail * (b1 - b0);
+    const int off_pre = wave_excl_scan(mine_pre, lane);
+    owner = __builtin_ctzll(__ballot(j >= off_pre && j < off_pre + mine_pre));
+    j -= __shfl(off_pre, owner);
+  }
+  int fb = 0, fk = 0, fL = 0, fslot = 0;
   if (lane == owner) {
-    int o = off;
+    int o = off, jj = j;
     for (int b = b0; b < b1; ++b) {
       const int L = len_of(b - b0, b);
-      const int sb = splits_for_budget(pre_blocks(L), t) + tail;
-      if (wi < o + sb) {
+      const int spre = splits_for_budget(pre_blocks(L), t);
+      if (wi < ntail ? b == wi / tail : jj < spre) {
         fb = b;
-        fk = wi - o;
+        fk = wi < ntail ? spre + wi % tail : jj;
         fL = L;
+        fslot = o + fk;
         break;
       }
-      o += sb;
+      jj -= spre;
+      o += spre + tail;
     }
   }
   it.b = __shfl(fb, owner);
   it.k = __shfl(fk, owner);
+  it.slot = __shfl(fslot, owner);
   const int L = __shfl(fL, owner);
   const int spre = splits_for_budget(pre_blocks(L), t);
   it.s_b = spre + tail;
@@ -669,14 +685,30 @@ void split_kernel(SplitParams p) {
   // contiguous run of (work item, head group) pairs in work-item-major order,
   // so that the splits of a sequence share one L2 for their queries, and the
   // head groups of a work item its cache rows.
+  //
+  // With several query tokens (main pass) the workgroups come in two kinds,
+  // the full-length prefix splits and the one-tile tails (work items below
+  // tail * B, see plan_item); each XCD gets an even share of each kind, the
+  // prefix splits first, so that the two head groups of a split start
+  // together and no XCD queues a full-length split behind another.  With one
+  // token this is the plain bijection above.
   int wi, hg;
   {
     const int ng = gridDim.y;
     const int total = gridDim.x * ng;
     const int flat = blockIdx.x + blockIdx.y * gridDim.x;
     const int xcd = flat & (kXcds - 1), idx = flat / kXcds;
-    const int q = total / kXcds, r = total % kXcds;
-    const int lin = xcd * q + min(xcd, r) + idx;
+    const int nt = REDO ? 0 : tail_splits(p.seqlen_q) * p.batch * ng;   // tail workgroups
+    const int nb = total - nt;                                         // the others
+    // Workgroups of each kind before XCD x, and on XCD x.
+    auto before = [&](int n, int x) { return x * (n / kXcds) + min(x, n % kXcds); };
+    const int nb_x = before(nb, xcd + 1) - before(nb, xcd);
+    int lin;
+    if (idx < nb_x) {
+      lin = nt + before(nb, xcd) + idx;
+    } else {   // XCD x's tails: the rest of its workgroups (never negative)
+      lin = (before(total, xcd) - before(nb, xcd)) + (idx - nb_x);
+    }
     wi = lin / ng;
     hg = lin - wi * ng;
   }
@@ -686,20 +718,36 @@ void split_kernel(SplitParams p) {
   const int g = lane >> 5;
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
-  // Rerun flag of this (work item, head group).  The main pass writes it for
-  // every workgroup of its grid; the rerun launch leaves at once when it is 0.
-  int32_t* const redo_flag = p.redo + (wi * (int)gridDim.y + hg);
+  // Rerun flags, one per (split slot, head group).  The main pass writes the
+  // flag of every split it runs (and of its workgroups past the end of the
+  // plan); the rerun launch, one workgroup per split slot, leaves at once
+  // when it is 0.
+  int32_t* redo_flag = p.redo + (wi * (int)gridDim.y + hg);
   if (REDO && *redo_flag == 0) return;
 
   // ---- work item (uniform) -------------------------------------------------
   // k: the split's index within its sequence; with several query tokens the
-  // last split (k = s_b - 1) is the tail, whose rows are masked per query row.
-  int b, k, r0, r1, s_b;
+  // last two splits are the tails, whose rows are masked per query row.
+  // split_slot (sequence-major) indexes the partials and rerun flags; in the
+  // main pass with tails, work items come tails first (see plan_item).
+  int b, k, r0, r1, s_b, split_slot = wi;
   if (p.num_split > 0) {
-    b = wi / p.num_split;
-    k = wi - b * p.num_split;
     s_b = p.num_split;
-    seq_split_range(clamp_len(p.seqlens[b], p.row_cap), p.seqlen_q, s_b - tail_splits(p.seqlen_q), k, &r0, &r1);
+    const int tl = tail_splits(p.seqlen_q), pre = s_b - tl;
+    if (!REDO && tl > 0) {
+      if (wi < tl * p.batch) {
+        b = wi / tl;
+        k = pre + wi % tl;
+      } else {
+        b = (wi - tl * p.batch) / pre;
+        k = (wi - tl * p.batch) - b * pre;
+      }
+      split_slot = b * s_b + k;
+    } else {
+      b = wi / s_b;
+      k = wi - b * s_b;
+    }
+    seq_split_range(clamp_len(p.seqlens[b], p.row_cap), p.seqlen_q, pre, k, &r0, &r1);
   } else if (!REDO) {
     const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
     if (!it.valid) {   // past the end of the plan
@@ -711,6 +759,7 @@ void split_kernel(SplitParams p) {
     r0 = it.r0;
     r1 = it.r1;
     s_b = it.s_b;
+    split_slot = it.slot;
   } else {
     // The plan the main pass published (the flag was set, so wi is in it).
     b = p.work[4 * wi + 0];
@@ -725,6 +774,8 @@ void split_kernel(SplitParams p) {
   if (p.seqlen_q > 1 && k >= s_b - tail_splits(p.seqlen_q))
     tail_lim = clamp_len(p.seqlens[b], p.row_cap) - (p.seqlen_q - 1);
   tail_lim = __builtin_amdgcn_readfirstlane(tail_lim);
+  split_slot = __builtin_amdgcn_readfirstlane(split_slot);
+  redo_flag = p.redo + (split_slot * (int)gridDim.y + hg);
   b = __builtin_amdgcn_readfirstlane(b);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
@@ -796,10 +847,10 @@ void split_kernel(SplitParams p) {
       for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
       if (g == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
     } else {
-      float* o = p.part_o + ((int64_t)wi * p.heads + h) * 512 + 4 * g;
+      float* o = p.part_o + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
 #pragma unroll
       for (int k = 0; k < 64; ++k) *reinterpret_cast<f32x4*>(o + 8 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g == 0) p.part_lse[(int64_t)wi * p.heads + h] = -__builtin_inff();
+      if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();
     }
     return;
   }
@@ -851,7 +902,7 @@ void split_kernel(SplitParams p) {
   // pass takes it from the first tile.
   float nmc = 0.f;
   if (REDO) {
-    const float m = p.part_lse[(int64_t)wi * p.heads + h];
+    const float m = p.part_lse[(int64_t)split_slot * p.heads + h];
     nmc = m == -__builtin_inff() ? 0.f : -(m * c);
   }
   float mx = -__builtin_inff();   // running max of all tiles seen (raw)
@@ -1054,7 +1105,7 @@ void split_kernel(SplitParams p) {
     const bool overflow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
     if (overflow) {
       if (wave == 0 && lane_t == 0) *redo_flag = 1;
-      if (head_ok_t && g_t == 0) p.part_lse[(int64_t)wi * p.heads + h_t] = mx;
+      if (head_ok_t && g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = mx;
       return;
     }
     if (wave == 0 && lane_t == 0) *redo_flag = 0;
@@ -1081,7 +1132,7 @@ void split_kernel(SplitParams p) {
     }
     if (g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
   } else {
-    float* o = p.part_o + ((int64_t)wi * p.heads + h_t) * 512;
+    float* o = p.part_o + ((int64_t)split_slot * p.heads + h_t) * 512;
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
@@ -1092,7 +1143,7 @@ void split_kernel(SplitParams p) {
         *reinterpret_cast<f32x4*>(o + v) = w;
       }
     }
-    if (g_t == 0) p.part_lse[(int64_t)wi * p.heads + h_t] = lse2;
+    if (g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
   }
 }
 

@@ -83,10 +83,14 @@ MLA_HD int32_t head_groups(int32_t heads) { return ceil_div(heads, kHeadsPerGrou
 
 // Most prefix splits the planner may emit (planner mode): one work item per
 // CU and head group, at least one per sequence.  The tail splits (one tile
-// each) come on top: they take a CU only briefly.
+// each) come on top, except that when they are at most a quarter of the
+// budget they are taken out of it: otherwise a few of them push the
+// workgroups just past one per CU, and on the XCDs where the extra one is a
+// full-length prefix split it waits for a whole second round.
 MLA_HD int32_t planner_cap(int32_t batch, int32_t heads, int32_t num_cus, int32_t seqlen_q) {
-  (void)seqlen_q;
-  const int32_t per_group = ceil_div(num_cus, head_groups(heads));
+  int32_t per_group = ceil_div(num_cus, head_groups(heads));
+  const int32_t tails = batch * tail_splits(seqlen_q);
+  if (tails > 0 && 4 * tails <= per_group) per_group -= tails;
   return batch > per_group ? batch : per_group;
 }
 

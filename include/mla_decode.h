@@ -132,7 +132,8 @@ typedef struct mla_desc {
  * How s_b is chosen (num_split == 0, "planner" mode) is this library's own
  * rule, meant to fill the compute units: one work item per CU is the target,
  * so the planner finds the smallest per-item block budget t with
- *   sum_b max(1, ceil(nb_b / t)) <= max(B, ceil(num_cus / head_groups))
+ *   sum_b max(1, ceil(nb_b / t)) <= max(B, C),  C = ceil(num_cus / head_groups)
+ * (C minus the 2B tail splits when seqlen_q > 1 and 8B <= C)
  * and sets s_b = max(1, ceil(nb_b / t)) (+2 for the tails), the prefix count
  * capped at MLA_MAX_SPLITS.  head_groups = ceil(H / 128) with H the query
  * rows; nb_b counts the prefix's blocks (the tails, one tile each, come on top).
@@ -147,7 +148,7 @@ int mla_num_cus(int device, int32_t* num_cus_out /* host */);
  * Upper bound on the work items a plan can have for this description
  * (tail = 2 when desc->seqlen_q > 1, else 0):
  *   num_split > 0 : B * (num_split + tail)
- *   num_split == 0: max(B, ceil(num_cus / head_groups)) + B * tail
+ *   num_split == 0: max(B, C) + B * tail, C as above
  */
 int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32_t* max_work_out /* host */);
 

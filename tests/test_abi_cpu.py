@@ -148,14 +148,18 @@ def test_empty_batch_is_ok_without_touching_memory(L):
 
 def test_workspace_size_formula(L):
     for B, H, ns, cus, sq in [(2, 16, 1, 256, 1), (64, 128, 0, 256, 1), (2, 128, 64, 256, 1), (3, 200, 0, 256, 1),
-                              (500, 128, 0, 256, 1), (64, 256, 0, 256, 2), (3, 96, 5, 256, 3), (200, 128, 0, 256, 4)]:
+                              (500, 128, 0, 256, 1), (64, 256, 0, 256, 2), (3, 96, 5, 256, 3), (200, 128, 0, 256, 4),
+                              (2, 256, 0, 256, 2), (16, 128, 0, 256, 4)]:
         d = _desc(B=B, H=H)
         d.seqlen_q = sq
         w = ctypes.c_int32()
         assert L.mla_max_work(ctypes.byref(d), ns, cus, ctypes.byref(w)) == 0
         hg = -(-H // 128)
         tail = 2 if sq > 1 else 0
-        want_w = B * (ns + tail) if ns else max(B, -(-cus // hg)) + B * tail
+        C = -(-cus // hg)
+        if tail and 4 * B * tail <= C:
+            C -= B * tail
+        want_w = B * (ns + tail) if ns else max(B, C) + B * tail
         assert w.value == want_w
         n = ctypes.c_size_t()
         assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0

@@ -259,3 +259,29 @@ def test_split_starts_keep_tiles_inside_pages():
         nsa, off, work = _plan(lens, heads, ns, int(rng.choice([80, 256, 304])), sq)
         nonempty = work[:, 3] > work[:, 2]
         assert (work[nonempty, 2] % 32 == 0).all(), (sq, ns, work[nonempty][work[nonempty, 2] % 32 != 0][:3])
+
+
+def test_xcd_mapping_with_two_kinds_is_a_bijection():
+    """The split kernel's workgroup order (restated): workgroup f runs on XCD
+    f % 8 as its (f // 8)-th; each XCD takes its even share of the nb prefix
+    workgroups first, then the rest of its workgroups are tails.  For every
+    total and tail count this must hit each work-item index exactly once,
+    tails in [0, nt) and prefix splits in [nt, total)."""
+    def before(n, x):
+        return x * (n // 8) + min(x, n % 8)
+
+    for total in list(range(1, 130)) + [255, 256, 257, 264, 512, 768, 1031]:
+        for nt in sorted({0, 1, 2, 7, 8, 9, total // 3, total // 2, total - 1, total} & set(range(total + 1))):
+            nb = total - nt
+            seen = []
+            for f in range(total):
+                x, idx = f % 8, f // 8
+                nb_x = before(nb, x + 1) - before(nb, x)
+                if idx < nb_x:
+                    lin = nt + before(nb, x) + idx
+                    assert nt <= lin < total
+                else:
+                    lin = before(total, x) - before(nb, x) + (idx - nb_x)
+                    assert 0 <= lin < nt
+                seen.append(lin)
+            assert sorted(seen) == list(range(total)), (total, nt)

@@ -54,7 +54,9 @@ Layout layout(const mla_desc* d, int32_t max_work) {
   L.redo = L.work + 4 * W * 4;
   L.part_lse = round_up(L.redo + W * (size_t)mla::head_groups(d->heads) * 4, 256);
   L.part_o = round_up(L.part_lse + W * H * 4, 256);
-  L.total = round_up(L.part_o + W * H * 512 * 4, 256);
+  // Partial outputs: fp16 for fp16 inputs (the output's precision), fp32 for bf16.
+  const size_t part_elt = d->dtype == MLA_DTYPE_F16 ? 2 : 4;
+  L.total = round_up(L.part_o + W * H * 512 * part_elt, 256);
   return L;
 }
 
@@ -309,7 +311,7 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   int32_t* work = reinterpret_cast<int32_t*>(ws + L.work);
   int32_t* redo = reinterpret_cast<int32_t*>(ws + L.redo);
   float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
-  float* part_o = reinterpret_cast<float*>(ws + L.part_o);
+  void* part_o = ws + L.part_o;
 
   // In planner mode the split kernel plans for itself (no planner launch).
   mla::SplitParams sp{};

@@ -21,7 +21,7 @@ struct SplitParams {
   int32_t* redo;                // [max_work][head groups]: main pass overflowed, rerun with the exact max
   uint16_t* out;
   float* lse;
-  float* part_o;                // [max_work, H, 512]
+  void* part_o;                 // [max_work, H, 512]: fp16 for fp16 inputs, else fp32
   float* part_lse;              // [max_work, H], base 2
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
@@ -38,7 +38,7 @@ struct SplitParams {
 };
 
 struct CombineParams {
-  const float* part_o;
+  const void* part_o;           // fp16 for fp16 inputs, else fp32
   const float* part_lse;
   const int32_t* split_offset;  // planner mode
   uint16_t* out;

@@ -846,8 +846,13 @@ void split_kernel(SplitParams p) {
 #pragma unroll
       for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
       if (g == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
+    } else if constexpr (DT == MLA_DTYPE_F16) {
+      uint16_t* o = static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
+      if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();
     } else {
-      float* o = p.part_o + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
+      float* o = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
 #pragma unroll
       for (int k = 0; k < 64; ++k) *reinterpret_cast<f32x4*>(o + 8 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();
@@ -1131,8 +1136,25 @@ void split_kernel(SplitParams p) {
       }
     }
     if (g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
+  } else if constexpr (DT == MLA_DTYPE_F16) {
+    // fp16 inputs: the normalised partial is kept in fp16, the output's own
+    // precision (one more rounding of at most 2^-12 of |O_k| before the
+    // weighted average); half the bytes of fp32 to write and to combine.
+    uint16_t* o = static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h_t) * 512;
+#pragma unroll
+    for (int vb = 0; vb < 16; ++vb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = 32 * vb + 8 * q + 4 * g_t;
+        u32x2 w;
+        w.x = pack2<DT>(acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv);
+        w.y = pack2<DT>(acc[vb][4 * q + 2] * inv, acc[vb][4 * q + 3] * inv);
+        *reinterpret_cast<u32x2*>(o + v) = w;
+      }
+    }
+    if (g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
   } else {
-    float* o = p.part_o + ((int64_t)split_slot * p.heads + h_t) * 512;
+    float* o = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h_t) * 512;
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
@@ -1177,6 +1199,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += mov_dpp_f32<0x141>(v);
   v += mov_dpp_f32<0x140>(v);
   return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+
+// Eight values of a partial row (element offset e): fp16 partials (fp16
+// inputs) in one 16-byte read, fp32 partials in two.
+template <int DT>
+__device__ __forceinline__ void load_part8(const void* part_o, int64_t e, f32x4& v0, f32x4& v1) {
+  if constexpr (DT == MLA_DTYPE_F16) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(part_o) + e);
+    v0 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.x, w.y}), f32x4);
+    v1 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.z, w.w}), f32x4);
+  } else {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(part_o) + e);
+    v0 = src[0];
+    v1 = src[1];
+  }
 }
 
 constexpr int kCombineUnroll = 8;   // splits per wave whose reads are in flight together (one wave per head)
@@ -1231,19 +1269,15 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
   constexpr int U = S ? S : kCombineUnroll;
   const int s = S ? S : s_rt;
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
-  const int64_t stride = (int64_t)p.heads * 512;   // floats between consecutive splits
-  const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
+  const int64_t stride = (int64_t)p.heads * 512;   // elements between consecutive splits
+  const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
   // Lane k holds the lse of split k (and k + 64).  The first U partial rows
   // are read in the same round trip: they do not depend on the weights.
   const float l0 = lane_lse(L, p.heads, s, lane);
   const float l1 = S ? -__builtin_inff() : lane_lse(L, p.heads, s, lane + 64);
   f32x4 v0[U], v1[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)u * stride);
-    v0[u] = src[0];
-    v1[u] = src[1];
-  }
+  for (int u = 0; u < U; ++u) load_part8<DT>(p.part_o, O + (int64_t)u * stride, v0[u], v1[u]);
   __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
   const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -1261,9 +1295,7 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = k0 + u < s ? k0 + u : s - 1;
-        const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
-        v0[u] = src[0];
-        v1[u] = src[1];
+        load_part8<DT>(p.part_o, O + (int64_t)k * stride, v0[u], v1[u]);
         lk[u] = L[(int64_t)k * p.heads];
       }
 #pragma unroll
@@ -1322,8 +1354,8 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 
   constexpr int U = kSplitkBatch;
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
-  const int64_t stride = (int64_t)p.heads * 512;   // floats between consecutive splits
-  const float* O = p.part_o + ((int64_t)base * p.heads + h) * 512 + 8 * lane;
+  const int64_t stride = (int64_t)p.heads * 512;   // elements between consecutive splits
+  const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
   const float l0 = lane_lse(L, p.heads, s, lane), l1 = lane_lse(L, p.heads, s, lane + 64);
   // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
   // s re-read split s - 1, which then gets weight 0.
@@ -1333,9 +1365,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
-      const f32x4* src = reinterpret_cast<const f32x4*>(O + (int64_t)k * stride);
-      v0[u] = src[0];
-      v1[u] = src[1];
+      load_part8<DT>(p.part_o, O + (int64_t)k * stride, v0[u], v1[u]);
       lk[u] = L[(int64_t)k * p.heads];
     }
   };

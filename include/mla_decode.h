@@ -156,7 +156,8 @@ int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32
  * Bytes of device workspace mla_decode needs for this description:
  *   plan (int32): B + (B+1) + 4*max_work, then max_work * ceil(H/128)
  *   rerun flags, rounded to 256 bytes; partial lse (fp32, base 2): max_work * H, rounded to 256;
- *   partial out (fp32): max_work * H * 512, rounded to 256.
+ *   partial out: max_work * H * 512 values, rounded to 256 bytes; fp16 for fp16
+ *   inputs (the output's precision), fp32 for bf16 inputs.
  */
 int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
 

@@ -150,7 +150,7 @@ def test_workspace_size_formula(L):
     for B, H, ns, cus, sq in [(2, 16, 1, 256, 1), (64, 128, 0, 256, 1), (2, 128, 64, 256, 1), (3, 200, 0, 256, 1),
                               (500, 128, 0, 256, 1), (64, 256, 0, 256, 2), (3, 96, 5, 256, 3), (200, 128, 0, 256, 4),
                               (2, 256, 0, 256, 2), (16, 128, 0, 256, 4)]:
-        d = _desc(B=B, H=H)
+        d = _desc(B=B, H=H, dtype=(B + H) % 2)   # fp16 and bf16 both covered
         d.seqlen_q = sq
         w = ctypes.c_int32()
         assert L.mla_max_work(ctypes.byref(d), ns, cus, ctypes.byref(w)) == 0
@@ -167,7 +167,7 @@ def test_workspace_size_formula(L):
         plan = 4 * B + 4 * (B + 1) + 16 * want_w + 4 * want_w * hg
         part_lse = r(plan)
         part_o = r(part_lse + 4 * want_w * H)
-        assert n.value == r(part_o + 2048 * want_w * H)
+        assert n.value == r(part_o + 512 * (2 if d.dtype == 0 else 4) * want_w * H)   # fp16 partials for fp16
 
 
 def _plan(lens, heads, ns, cus, sq=1):

@@ -1,0 +1,40 @@
+"""The benchmark's algorithmic work figures and bound choice (CPU only)."""
+import numpy as np
+
+import bench
+
+
+def test_headline_figures():
+    # 64 sequences of 4096 rows, 128 heads: 1152 B per cache row and per Q row,
+    # 1024 B of out and 4 B of lse per (b, h); 2 * 128 * (576 + 512) flop per row.
+    flops, kv, total = bench.workload_figures([4096] * 64, 128)
+    assert kv == 64 * 4096 * 1152
+    assert total == kv + 64 * 128 * (1152 + 1024 + 4)
+    assert flops == 2 * 128 * 1088 * 64 * 4096
+
+
+def test_several_tokens_visible_rows():
+    # Two tokens of 16 heads each over 5 rows: token 0 sees 4 rows, token 1 sees 5.
+    flops, kv, total = bench.workload_figures([5], 32, seqlen_q=2)
+    assert flops == 2 * 16 * 1088 * (4 + 5)
+    assert kv == 5 * 1152
+    # Negative lengths count as empty sequences.
+    f0, kv0, _ = bench.workload_figures([-3, 0], 8)
+    assert f0 == 0 and kv0 == 0
+
+
+def test_bound_follows_intensity():
+    # One token per sequence at H = 128 sits below the ridge (2.5 PF / 8 TB/s = 312.5
+    # flop/B): HBM binds.  Two tokens double the flops per row: MFMA binds.
+    for s, want in [(1, "hbm"), (2, "mfma")]:
+        flops, _, total = bench.workload_figures([4096] * 64, 128 * s, seqlen_q=s)
+        first, other = bench.split_bounds(flops, total, 0.1, None)
+        assert first["bound"] == want and other["bound"] != want
+        hbm = first if want == "hbm" else other
+        mfma = other if want == "hbm" else first
+        assert np.isclose(hbm["achieved"], total / 1e-4 / 1e9, rtol=1e-4)
+        assert np.isclose(mfma["achieved"], flops / 1e-4 / 1e12, rtol=1e-4)
+        assert np.isclose(hbm["frac"], hbm["achieved"] / 8000.0, atol=1e-4)
+    # No launch time: no figures, but the bound is still named.
+    first, _ = bench.split_bounds(1.0, 1.0, 0.0, 123)
+    assert first["achieved"] is None and first["frac"] is None and first["traffic"] == 123

@@ -896,6 +896,8 @@ void split_kernel(SplitParams p) {
       __syncthreads();
       if (lane == 0) flags[wave] = 0;
       __syncthreads();
+    } else {
+      __syncthreads();   // the other waves' barrier before their epilogue
     }
     return;
   }
@@ -1121,51 +1123,70 @@ void split_kernel(SplitParams p) {
   const bool nonempty = ltot > 0.f;
   const float inv = nonempty ? 1.f / ltot : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) - nmc : -__builtin_inff();
-  if (!head_ok_t) return;
-  if (s_b == 1) {
-    uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h_t * p.out_sh;
+  if (head_ok_t && g_t == 0) {
+    if (s_b == 1) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
+    else p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
+  }
+  // The rows leave through LDS: each wave stages its 32 head rows in a
+  // region of its own (past the overflow words), then writes one whole row
+  // (1 KiB, 16 bytes per lane) per store instruction.  Straight from the
+  // accumulator layout, a store would cover 16-byte pieces of 32 rows.
+  // Staged 16-byte chunk c of row r sits at chunk c ^ r: the accumulator
+  // writes (32 rows) and the row reads (64 chunks of one row) are both free
+  // of bank conflicts.  Every wave has finished with the tile ring: the main
+  // pass passed the two barriers around the overflow words; the rerun passes
+  // this one (idle waves pass it too).
+  if (REDO) __syncthreads();
+  lds_char* stage = lds + 256 + wave * 32768;
+  const int hl_t = lane_t & 31;
+  auto stage_at = [&](int row, int chunk) __attribute__((always_inline)) {
+    return stage + row * 1024 + ((chunk ^ row) << 4);
+  };
+  if (s_b == 1 || DT == MLA_DTYPE_F16) {
+    // 16-bit rows (the output, or the fp16 partial: the output's own
+    // precision, one more rounding of at most 2^-12 of |O_k| before the
+    // weighted average): 512 values = 64 chunks of 8; this lane holds
+    // values 8 q + 4 g .. + 3 of chunk 4 vb + q.
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int v = 32 * vb + 8 * q + 4 * g_t;
         u32x2 w;
         w.x = pack2<DT>(acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv);
         w.y = pack2<DT>(acc[vb][4 * q + 2] * inv, acc[vb][4 * q + 3] * inv);
-        *reinterpret_cast<u32x2*>(o + v) = w;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage_at(hl_t, 4 * vb + q) + 8 * g_t) = w;
       }
     }
-    if (g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
-  } else if constexpr (DT == MLA_DTYPE_F16) {
-    // fp16 inputs: the normalised partial is kept in fp16, the output's own
-    // precision (one more rounding of at most 2^-12 of |O_k| before the
-    // weighted average); half the bytes of fp32 to write and to combine.
-    uint16_t* o = static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h_t) * 512;
-#pragma unroll
-    for (int vb = 0; vb < 16; ++vb) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v = 32 * vb + 8 * q + 4 * g_t;
-        u32x2 w;
-        w.x = pack2<DT>(acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv);
-        w.y = pack2<DT>(acc[vb][4 * q + 2] * inv, acc[vb][4 * q + 3] * inv);
-        *reinterpret_cast<u32x2*>(o + v) = w;
-      }
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      if (h0 + r >= p.heads) break;
+      uint16_t* row = s_b == 1 ? p.out + (int64_t)b * p.out_sb + (int64_t)(h0 + r) * p.out_sh
+                               : static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h0 + r) * 512;
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage_at(r, lane_t));
+      *reinterpret_cast<u32x4*>(row + 8 * lane_t) = v;
     }
-    if (g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
   } else {
-    float* o = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h_t) * 512;
+    // fp32 partial rows (bf16 inputs), in two halves of 256 values = 64
+    // chunks of 4; this lane holds chunk 8 (vb % 8) + 2 q + g.
 #pragma unroll
-    for (int vb = 0; vb < 16; ++vb) {
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v = 32 * vb + 8 * q + 4 * g_t;
-        f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
-                   acc[vb][4 * q + 3] * inv};
-        *reinterpret_cast<f32x4*>(o + v) = w;
+      for (int vb = 8 * half; vb < 8 * half + 8; ++vb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
+                           acc[vb][4 * q + 3] * inv};
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage_at(hl_t, 8 * (vb & 7) + 2 * q + g_t)) = w;
+        }
+      }
+#pragma unroll 4
+      for (int r = 0; r < 32; ++r) {
+        if (h0 + r >= p.heads) break;
+        float* row = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h0 + r) * 512 + 256 * half;
+        const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(stage_at(r, lane_t));
+        *reinterpret_cast<f32x4*>(row + 4 * lane_t) = v;
       }
     }
-    if (g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
   }
 }
 

@@ -356,6 +356,8 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   int hi = maxnb > 1 ? maxnb : 1;
   int64_t lo64 = (sumnb + cap - 1) / cap;
   int lo = (int)(lo64 < 1 ? 1 : (lo64 > hi ? hi : lo64));
+  // Equal lengths meet the cap at the lower bound: one probe instead of a search.
+  if (lo < hi && wave_sum_i32(lane_splits(lo)) <= cap) hi = lo;
   while (lo < hi) {
     const int mid = lo + (hi - lo) / 2;
     if (wave_sum_i32(lane_splits(mid)) <= cap) hi = mid;

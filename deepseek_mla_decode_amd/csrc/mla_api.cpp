@@ -272,8 +272,10 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     if (s < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride %lld", (long long)s);
     if (s % 8) return fail(MLA_ERR_UNSUPPORTED, "stride %lld is not a multiple of 8 elements", (long long)s);
   }
-  if (d->kv_sr >= MLA_MAX_ROW_STRIDE || d->kpe_sr >= MLA_MAX_ROW_STRIDE)
-    return fail(MLA_ERR_UNSUPPORTED, "cache row strides must be below %d elements", MLA_MAX_ROW_STRIDE);
+  if (d->kv_sr >= MLA_MAX_ROW_STRIDE || d->kpe_sr >= MLA_MAX_ROW_STRIDE || d->q_nope_sh >= MLA_MAX_ROW_STRIDE ||
+      d->q_pe_sh >= MLA_MAX_ROW_STRIDE)
+    return fail(MLA_ERR_UNSUPPORTED, "cache row and query head strides must be below %d elements",
+                MLA_MAX_ROW_STRIDE);
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(kv_latent, 16) || !aligned(k_pe, 16) ||
       !aligned(out, 16))
     return fail(MLA_ERR_UNSUPPORTED, "q/cache/out pointers must be 16-byte aligned");

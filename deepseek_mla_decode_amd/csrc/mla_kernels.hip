@@ -583,23 +583,6 @@ __device__ __forceinline__ void issue_part(const DmaCursor& c, const DmaTile& d,
   }
 }
 
-// Q slice of this lane's head: k-step s (dims 16s .. 16s+15, half g of them)
-// is the B operand of the score MFMA.  The 32 latent k-steps stay in VGPRs
-// for the whole work item; the 4 RoPE k-steps go to this wave's LDS slots
-// (16 bytes per lane, [step][wave][lane]).
-__device__ __forceinline__ void load_q(const SplitParams& p, int b, int h, bool head_ok, int wave, int lane,
-                                       lds_char* qlds, u32x4 (&qreg)[kQRegSteps]) {
-  const int g = lane >> 5;
-  const uint16_t* qn = p.q_nope + (int64_t)b * p.q_nope_sb + (int64_t)h * p.q_nope_sh + 8 * g;
-  const uint16_t* qp = p.q_pe + (int64_t)b * p.q_pe_sb + (int64_t)h * p.q_pe_sh + 8 * g;
-#pragma unroll
-  for (int s = 0; s < 36; ++s) {
-    u32x4 v = s < 32 ? ld16(qn + 16 * s) : ld16(qp + 16 * (s - 32));
-    v = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
-    if (s < kQRegSteps) qreg[s < kQRegSteps ? s : 0] = v;
-    else *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(qlds + (((s - kQRegSteps) * 4 + wave) * 64 + lane) * 16) = v;
-  }
-}
 
 // Softmax of one score tile, cut into steps so that the loop can run them one
 // or two instructions at a time between MFMAs.  x[] holds the raw scores
@@ -791,7 +774,6 @@ void split_kernel(SplitParams p) {
   const int h = head_ok ? h0 + hl : p.heads - 1;
 
   u32x4 qreg[kQRegSteps];
-  load_q(p, b, h, head_ok, wave, lane, qlds, qreg);
   // This wave's Q RoPE slots: qlds + 1024 wave + 16 lane (+ 4096 per k-step).
   const uint32_t qwave = lds_u32(qlds) + 1024u * (uint32_t)wave;
 
@@ -861,6 +843,45 @@ void split_kernel(SplitParams p) {
     }
     return;
   }
+
+  // Queries.  A wave's 32 heads x 576 values have the shape of a cache tile
+  // (32 rows of 512 latent + 64 RoPE values), so the wave loads them like
+  // one, into ring slot `wave` with the tile's layout and swizzle: every load
+  // moves one whole 1 KiB row (or the RoPE parts of 8 rows), where loading
+  // each lane's operand straight from memory would touch 32 rows per load.
+  // The score MFMA's B operand (head hl, k-step s, half g) then sits exactly
+  // where its A operand would for cache row hl, so the K-read addresses give
+  // it.  The 32 latent k-steps stay in VGPRs for the whole work item; the 4
+  // RoPE k-steps go to this wave's LDS slots (16 bytes per lane,
+  // [step][wave][lane]).  Heads past the last compute with a zero query.  The
+  // barrier keeps the tile loads out of the ring until every wave has read
+  // its queries.
+  if (h0 < p.heads) {
+    DmaCursor qc{};
+    qc.lat_rb = (uint32_t)(p.q_nope_sh * 2);
+    qc.rope_rb = (uint32_t)(p.q_pe_sh * 2);
+    DmaTile qd;
+    qd.lat = reinterpret_cast<const char*>(p.q_nope + (int64_t)b * p.q_nope_sb + (int64_t)h0 * p.q_nope_sh);
+    qd.rope = reinterpret_cast<const char*>(p.q_pe + (int64_t)b * p.q_pe_sb + (int64_t)h0 * p.q_pe_sh);
+    qd.nlast = min(31, p.heads - 1 - h0);
+    qd.lds = lds_u32(slot(wave));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int part = 0; part < kLoadsPerTile; ++part) issue_part(qc, qd, w, lane16, part);
+    }
+    wait_cnt<0, 15>();
+    const uint32_t base = qd.lds;
+#pragma unroll
+    for (int st = 0; st < 36; ++st) {
+      u32x4 v = st < 32 ? lds_get16(lds_at(xor_add(base, 32u * (st & 7), klx)), 256 * (st >> 3))
+                        : lds_get16(lds_at(xor_add(base, 32u * (st - 32), rkx)), 0);
+      v = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
+      if (st < kQRegSteps) qreg[st < kQRegSteps ? st : 0] = v;
+      else *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(qlds + (((st - kQRegSteps) * 4 + wave) * 64 + lane) * 16) = v;
+    }
+  }
+  __syncthreads();
 
   // A wave whose 32 heads all lie past the last head (few heads per group)
   // computes nothing: it only issues its share of every tile's loads and

@@ -61,14 +61,16 @@ typedef enum mla_dtype {
 #define MLA_SPLIT_BLOCK_ROWS 64
 /* Largest number of splits of one sequence. */
 #define MLA_MAX_SPLITS 1024
-/* Cache row strides (kv_sr, kpe_sr) must be below this many elements: the
- * kernel forms in-tile row offsets (31 rows) in 32-bit and 24-bit arithmetic. */
+/* Cache row strides (kv_sr, kpe_sr) and query head strides (q_nope_sh,
+ * q_pe_sh) must be below this many elements: the kernel forms in-tile row
+ * offsets (31 rows or heads) in 32-bit and 24-bit arithmetic. */
 #define MLA_MAX_ROW_STRIDE (1 << 22)
 
 /*
  * Problem description.  All strides are in ELEMENTS of the input dtype and must
- * keep every row start 16-byte aligned (multiples of 8 elements); kv_sr and
- * kpe_sr must be below MLA_MAX_ROW_STRIDE (MLA_ERR_UNSUPPORTED otherwise).
+ * keep every row start 16-byte aligned (multiples of 8 elements); kv_sr,
+ * kpe_sr, q_nope_sh and q_pe_sh must be below MLA_MAX_ROW_STRIDE
+ * (MLA_ERR_UNSUPPORTED otherwise).
  *
  * Contiguous cache (block_table == NULL):
  *   kv_latent[b, j, 0, :] at kv_latent + b*kv_sb + j*kv_sr      (512 values)

@@ -84,6 +84,7 @@ def _decode(L, desc, num_split=0, scale=1 / 24, ptrs=None, block_table=None, ws=
     ("zero_scale", _lib.MLA_ERR_INVALID_ARG),
     ("neg_scale", _lib.MLA_ERR_INVALID_ARG),
     ("huge_row_stride", _lib.MLA_ERR_UNSUPPORTED),
+    ("huge_q_head_stride", _lib.MLA_ERR_UNSUPPORTED),
 ])
 def test_validation_errors(L, case, expect):
     d = _desc()
@@ -136,6 +137,8 @@ def test_validation_errors(L, case, expect):
         kw["scale"] = -0.04
     elif case == "huge_row_stride":
         d.kpe_sr = 1 << 22
+    elif case == "huge_q_head_stride":
+        d.q_pe_sh = 1 << 22
     st = _decode(L, d, **kw)
     assert st == expect, (case, st, L.mla_last_error())
     assert L.mla_last_error().decode()

@@ -178,24 +178,29 @@ def test_run_to_run_bitwise_deterministic(mla, dtype, paged):
         assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
-def test_strided_tensors(mla):
+@pytest.mark.parametrize("dtype,heads,ns", [("f16", 64, 2), ("f16", 128, 1), ("bf16", 128, 3), ("bf16", 100, 0)])
+def test_strided_tensors(mla, dtype, heads, ns):
+    """Queries as slices of wider buffers (head strides 1024 and 128 values),
+    the output written into a strided view whose guard bands must stay
+    untouched: the queries are loaded row by row and the output leaves row by
+    row, so both must follow the strides exactly (partial head groups too)."""
     import torch
     from mla_inputs.torch_io import from_device, to_device
-    inp = mi.make_contiguous(3, 64, 96, [96, 50, 7], "f16", seed=108)
+    inp = mi.make_contiguous(3, heads, 200, [200, 50, 7], dtype, seed=108)
     d = to_device(inp, "cuda")
-    # Queries as slices of a wider buffer, output into a strided view.
-    qbig = torch.zeros((3, 64, 1024), dtype=torch.float16, device="cuda")
+    tdt = d["q_nope"].dtype
+    qbig = torch.zeros((3, heads, 1024), dtype=tdt, device="cuda")
     qbig[:, :, 256:768] = d["q_nope"]
-    qpe_big = torch.zeros((3, 64, 128), dtype=torch.float16, device="cuda")
+    qpe_big = torch.zeros((3, heads, 128), dtype=tdt, device="cuda")
     qpe_big[:, :, 64:] = d["q_pe"]
-    obig = torch.full((3, 64, 640), 7.0, dtype=torch.float16, device="cuda")
+    obig = torch.full((3, heads, 640), 7.0, dtype=tdt, device="cuda")
     out = obig[:, :, 64:576]
-    lse = torch.empty((3, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((3, heads), dtype=torch.float32, device="cuda")
     mla.mla_decode(qbig[:, :, 256:768], qpe_big[:, :, 64:], d["kv_latent"], d["k_pe"], None,
-                   d["cache_seqlens"], inp.softmax_scale, num_split=2, out=out, lse=lse)
+                   d["cache_seqlens"], inp.softmax_scale, num_split=ns, out=out, lse=lse)
     torch.cuda.synchronize()
     ro, rl = oracle.mla_decode_ref(inp)
-    assert_parity(from_device(out), from_device(lse), ro, rl, "strided")
+    assert_parity(from_device(out), from_device(lse), ro, rl, f"strided {dtype} H={heads} split={ns}")
     assert (obig[:, :, :64] == 7).all() and (obig[:, :, 576:] == 7).all()
 
 

@@ -354,7 +354,7 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   // is at least sum_b nb_b / t, so t starts at ceil(sum nb / cap).
   const int cap = planner_cap(B, p.heads, p.num_cus, sq);
   int hi = maxnb > 1 ? maxnb : 1;
-  int64_t lo64 = (sumnb + cap - 1) / cap;
+  const int64_t lo64 = sumnb < (1 << 30) && cap < (1 << 30) ? ceil_div_small((int)sumnb, cap) : (sumnb + cap - 1) / cap;
   int lo = (int)(lo64 < 1 ? 1 : (lo64 > hi ? hi : lo64));
   // Equal lengths meet the cap at the lower bound: one probe instead of a search.
   if (lo < hi && wave_sum_i32(lane_splits(lo)) <= cap) hi = lo;

@@ -23,6 +23,12 @@ constexpr int kMaxSplits = 1024;
 constexpr int kHeadsPerGroup = 128;
 
 MLA_HD int32_t ceil_div(int32_t a, int32_t b) { return (int32_t)(((int64_t)a + b - 1) / b); }
+// ceil(a / b) for 0 <= a < 2^30 and 1 <= b < 2^30, in 32-bit unsigned
+// arithmetic: the planner's inner loops run on every wave of the split kernel,
+// where a 64-bit divide expands to a long instruction sequence.
+MLA_HD int32_t ceil_div_small(int32_t a, int32_t b) {
+  return (int32_t)(((uint32_t)a + (uint32_t)b - 1u) / (uint32_t)b);
+}
 
 MLA_HD int32_t clamp_len(int32_t L, int32_t cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
@@ -75,7 +81,7 @@ MLA_HD void seq_split_range(int32_t L, int32_t seqlen_q, int32_t s_pre, int32_t 
 
 // Splits given to a sequence of nb blocks when each work item may take up to t blocks.
 MLA_HD int32_t splits_for_budget(int32_t nb, int32_t t) {
-  int32_t s = nb <= 0 ? 1 : ceil_div(nb, t);
+  int32_t s = nb <= 0 ? 1 : ceil_div_small(nb, t);   // nb <= 2^25 blocks, 1 <= t <= nb
   return s > kMaxSplits ? kMaxSplits : s;
 }
 

@@ -1360,10 +1360,25 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
   if (lane == 0) p.lse[(int64_t)b * p.heads + h] = cw.total * kLn2;
 }
 
+// Grid position (x, y) of this workgroup, remapped so that each XCD runs a
+// contiguous run of (x, y) in y-major order.  The split kernel gives each XCD
+// a contiguous run of work items, i.e. of sequences, so a sequence's partials
+// are then read on the XCD whose L2 took their writes.  A bijection of the
+// grid (the dispatcher deals flat ids to the XCDs round-robin).
+__device__ __forceinline__ void xcd_grid_pos(int& x, int& y) {
+  const int total = gridDim.x * gridDim.y;
+  const int flat = blockIdx.x + blockIdx.y * gridDim.x;
+  const int xcd = flat & (kXcds - 1), idx = flat / kXcds;
+  const int lin = xcd * (total / kXcds) + min(xcd, total % kXcds) + idx;
+  y = lin / gridDim.x;
+  x = lin - y * gridDim.x;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
-  const int b = blockIdx.y;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int hx, b;
+  xcd_grid_pos(hx, b);
+  const int h = hx * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (h >= p.heads) return;
   int s, base;
@@ -1390,7 +1405,8 @@ __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
 template <int DT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   __shared__ f32x4 red[4][2][64];   // [wave][half][lane]: 8 values per lane
-  const int h = blockIdx.x, b = blockIdx.y;
+  int h, b;
+  xcd_grid_pos(h, b);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int s, base;
   combine_range(p, b, s, base);

@@ -288,3 +288,37 @@ def test_xcd_mapping_with_two_kinds_is_a_bijection():
                     assert 0 <= lin < nt
                 seen.append(lin)
             assert sorted(seen) == list(range(total)), (total, nt)
+
+
+def test_combine_xcd_order_is_a_bijection_matching_the_split_order():
+    """The combine kernels' workgroup order (restated): workgroup (x, y) with
+    flat id f = x + y * gx runs on XCD f % 8 as its (f // 8)-th and takes grid
+    position lin = before(total, f % 8) + f // 8 in y-major order.  It must hit
+    every (x, y) exactly once, and with equal splits per sequence each XCD must
+    merge the sequences whose splits the split kernel gave it (the same
+    contiguous run of sequences)."""
+    def before(n, x):
+        return x * (n // 8) + min(x, n % 8)
+
+    for gx in (1, 2, 3, 8, 13, 32, 33, 128):
+        for gy in (1, 2, 5, 7, 8, 64, 100, 129):
+            total = gx * gy
+            seen = set()
+            for f in range(total):
+                lin = before(total, f % 8) + f // 8
+                seen.add((lin % gx, lin // gx))
+            assert seen == {(x, y) for x in range(gx) for y in range(gy)}, (gx, gy)
+    # B sequences of s splits: split workgroup f works on item before(B s, f % 8)
+    # + f // 8, sequence item // s; combine workgroups of sequence b sit on the
+    # XCDs whose split workgroups hold b.
+    for B, s, gx in ((64, 4, 32), (128, 2, 32), (2, 128, 128), (40, 6, 32)):
+        W = B * s
+        split_xcd = {}
+        for f in range(W):
+            item = before(W, f % 8) + f // 8
+            split_xcd.setdefault(item // s, set()).add(f % 8)
+        total = gx * B
+        for f in range(total):
+            b = (before(total, f % 8) + f // 8) // gx
+            if len(split_xcd[b]) == 1:
+                assert f % 8 in split_xcd[b], (B, s, b)

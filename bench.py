@@ -2,17 +2,23 @@
 """Benchmark of the MI355X MLA decode path (one GPU).
 
 A step is one full decode call (the split kernel, which plans its own work
-item; the exact-max rerun launch; the combine) over one batch of synthetic
-inputs already resident in HBM.  Default workload:
+item, and the combine) over one batch of synthetic inputs already resident in
+HBM.  Default workload:
 B=64, H=128, L=4096 for every sequence, fp16, contiguous cache, i.i.d. N(0,1)
 inputs, softmax_scale = 1/sqrt(576), planner-chosen splits.
 
 Prints ONE JSON line.  Throughput is TFLOPS of the algorithmic work
 2·H·(576 + 512) per valid cache row; the line also carries KV GB/s, µs per
 call, the fraction of the per-workload roofline min(8 TB/s × intensity, 2.5
-PFLOP/s dense fp16/bf16), the split kernel's launch time (from the launch's own
-dispatch events) against the HBM peak with its measured traffic (`roofline`),
-and the fp64 CPU oracle timed on a sample of the workload (`cpu_baseline`).
+PFLOP/s dense fp16/bf16), the split kernel against the HBM peak with its
+measured traffic (`roofline`), and the fp64 CPU oracle timed on a sample of
+the workload (`cpu_baseline`).
+
+Kernel times.  The timed region (events on the launch stream around K calls)
+gives the time of a call.  A second pass times each launch from its own
+dispatch events; those events slow the launches down by a few percent, so that
+pass only gives each kernel's share of the call, and a kernel's time is its
+share of the timed-region time (the per-kernel times add up to the call).
 """
 from __future__ import annotations
 
@@ -89,15 +95,35 @@ def split_bounds(flops: float, total_bytes: float, split_ms: float, traffic):
     return (hbm, mfma) if hbm_bound else (mfma, hbm)
 
 
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return n, model
+
+
 def cpu_baseline(inp, budget_s: float):
-    """Time the fp64 oracle on the first sequences of the workload until ~budget_s."""
-    import numpy as np
+    """Time the fp64 oracle on the first sequences of the workload until ~budget_s.
+    `cores` is the thread count of the BLAS pool the oracle's matrix products
+    run on (the rest of the oracle is single-threaded NumPy)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    nproc, model = host_cpu()
     done, t0 = 0, time.perf_counter()
     while done < inp.batch and time.perf_counter() - t0 < budget_s:
         oracle.mla_decode_ref(inp, batches=[done])
@@ -106,7 +132,8 @@ def cpu_baseline(inp, budget_s: float):
     flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads, inp.seqlen_q)
     return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} query rows), fp64 NumPy, "
-                      f"{el:.1f} s wall"}
+                      f"{el:.1f} s wall",
+            "host": {"nproc": nproc, "cpu_model": model}}
 
 
 def main() -> int:
@@ -187,15 +214,20 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # Per-kernel durations from HIP events recorded by the library on the launch stream.
+    # Each kernel's share of a call, from the launches' own dispatch events
+    # (a second pass; those events slow the launches, so only the shares are
+    # used), applied to the timed-region time of a call.
     mla.mla_timing_enable(True)
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    split_ms, rerun_ms, comb_ms, calls = mla.mla_timing_read()
+    split_ev, comb_ev, calls = mla.mla_timing_read()
     mla.mla_timing_enable(False)
-    split_avg = split_ms / max(calls, 1)
+    share = split_ev / (split_ev + comb_ev) if split_ev + comb_ev > 0 else 1.0
+    split_avg = ms * share
+    comb_avg = ms - split_avg
+    assert split_avg + comb_avg <= ms * (1 + 1e-9)
 
     check = None
     if args.check:
@@ -238,7 +270,10 @@ def main() -> int:
         "arith_intensity": round(ai, 1),
         "roofline_tflops": round(roof_tflops, 1),
         "frac_of_roofline": round(tflops / roof_tflops, 4),
-        "kernel_ms": {"split": split_avg, "rerun": rerun_ms / max(calls, 1), "combine": comb_ms / max(calls, 1)},
+        "kernel_ms": {"split": round(split_avg, 5), "combine": round(comb_avg, 5),
+                      "split_share": round(share, 4),
+                      "event_pass_ms": {"split": round(split_ev / max(calls, 1), 5),
+                                        "combine": round(comb_ev / max(calls, 1), 5)}},
         # The binding bound of the split kernel: HBM below the ridge intensity
         # (8 TB/s x intensity < 2.5 PFLOP/s, one query token per sequence), MFMA above it
         # (several query tokens share each cache row); the other bound beside it.

@@ -150,6 +150,8 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     torch = _torch()
     if not q_nope.is_cuda:
         raise ValueError("tensors must live on the GPU")
+    _check_placement(q_nope, dict(q_pe=q_pe, kv_latent=kv_latent, k_pe=k_pe, block_table=block_table,
+                                  cache_seqlens=cache_seqlens, out=out, lse=lse, workspace=workspace))
     seqlen_q, four_d = 1, q_nope.dim() == 4
     if four_d:
         B, seqlen_q, Hq = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
@@ -170,15 +172,14 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
         lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H):
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
-    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_contiguous():
-        raise ValueError("cache_seqlens must be a contiguous int32 tensor")
-    if block_table is not None and (block_table.dtype != torch.int32 or block_table.stride(1) != 1):
-        raise ValueError("block_table must be int32 with contiguous rows")
+    _check_batch_arrays(B, cache_seqlens, block_table)
     desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q)
     s = torch.cuda.current_stream(q_nope.device) if stream is None else stream
     if workspace is None:
         need = mla_workspace_size(desc, num_split, mla_num_cus(q_nope.device.index))
         workspace = _workspace(q_nope.device, s.cuda_stream, need)
+    elif not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
     kv = _as4(kv_latent, D_LATENT, "kv_latent")
     kp = _as4(k_pe, D_ROPE, "k_pe")
     st = _lib.lib().mla_decode(
@@ -190,6 +191,34 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     if four_d:
         return out4, lse4
     return out, lse
+
+
+def _check_placement(q_nope, tensors) -> None:
+    """Every tensor argument must live on q_nope's GPU: the C ABI takes raw
+    device addresses, so a host tensor's pointer would reach the kernels as a
+    host address (a GPU memory fault), and another GPU's as a foreign one."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != q_nope.device:
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on q_nope's device {q_nope.device}")
+
+
+def _check_batch_arrays(batch: int, cache_seqlens, block_table) -> None:
+    """cache_seqlens: contiguous int32 with exactly `batch` entries; block_table
+    (paged): int32 [rows >= batch, max_blocks] with contiguous rows.  The
+    kernels read cache_seqlens[0..B) and block_table rows 0..B-1, so shorter
+    arrays would be read past their end."""
+    import torch
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous int32 tensor")
+    if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] != batch:
+        raise ValueError(f"cache_seqlens must have shape [{batch}], got {tuple(cache_seqlens.shape)}")
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be a 2-D int32 tensor with contiguous rows")
+        if block_table.shape[0] < batch:
+            raise ValueError(f"block_table has {block_table.shape[0]} rows for a batch of {batch}")
 
 
 def _rows_view(t, name):
@@ -243,8 +272,8 @@ def mla_timing_enable(enable: bool = True) -> None:
 
 
 def mla_timing_read():
-    """(split_ms, rerun_ms, combine_ms, calls) summed since the last read."""
-    a, b, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    """(split_ms, combine_ms, calls) summed since the last read."""
+    a, c = ctypes.c_float(), ctypes.c_float()
     n = ctypes.c_int32()
-    _lib.check(_lib.lib().mla_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(n)))
-    return a.value, b.value, c.value, n.value
+    _lib.check(_lib.lib().mla_timing_read(ctypes.byref(a), ctypes.byref(c), ctypes.byref(n)))
+    return a.value, c.value, n.value

@@ -40,9 +40,9 @@ std::atomic<int32_t> g_num_cus[kMaxDevices];
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: [plan ints][rerun flags, one per (work item, head group)][partial lse fp32][partial out fp32].
+// Workspace layout: [plan ints][partial lse fp32][partial rows fp16][fp32 copies of wide rows].
 struct Layout {
-  size_t num_splits, split_offset, work, redo, part_lse, part_o, total;
+  size_t num_splits, split_offset, work, part_lse, part16, part32, total;
 };
 
 Layout layout(const mla_desc* d, int32_t max_work) {
@@ -51,12 +51,10 @@ Layout layout(const mla_desc* d, int32_t max_work) {
   L.num_splits = 0;
   L.split_offset = L.num_splits + B * 4;
   L.work = L.split_offset + (B + 1) * 4;
-  L.redo = L.work + 4 * W * 4;
-  L.part_lse = round_up(L.redo + W * (size_t)mla::head_groups(d->heads) * 4, 256);
-  L.part_o = round_up(L.part_lse + W * H * 4, 256);
-  // Partial outputs: fp16 for fp16 inputs (the output's precision), fp32 for bf16.
-  const size_t part_elt = d->dtype == MLA_DTYPE_F16 ? 2 : 4;
-  L.total = round_up(L.part_o + W * H * 512 * part_elt, 256);
+  L.part_lse = round_up(L.work + 4 * W * 4, 256);
+  L.part16 = round_up(L.part_lse + W * H * 4, 256);
+  L.part32 = round_up(L.part16 + W * H * 512 * 2, 256);
+  L.total = round_up(L.part32 + W * H * 512 * 4, 256);
   return L;
 }
 
@@ -96,10 +94,10 @@ int max_work_of(const mla_desc* d, int32_t num_split, int32_t num_cus, int32_t* 
 
 // ---- timing ----------------------------------------------------------------
 constexpr int kMaxTimed = 4096;
-constexpr int kEventsPerCall = 6;
+constexpr int kEventsPerCall = 4;
 std::mutex g_tmu;
 bool g_timing = false;
-std::vector<hipEvent_t> g_events;  // 6 per call: split, rerun, combine (start, stop)
+std::vector<hipEvent_t> g_events;  // 4 per call: split, combine (start, stop)
 std::vector<uint8_t> g_combined;   // per call: whether a combine ran (and its events were recorded)
 int g_timed = 0;
 
@@ -311,9 +309,9 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   int32_t* num_splits = reinterpret_cast<int32_t*>(ws + L.num_splits);
   int32_t* split_offset = reinterpret_cast<int32_t*>(ws + L.split_offset);
   int32_t* work = reinterpret_cast<int32_t*>(ws + L.work);
-  int32_t* redo = reinterpret_cast<int32_t*>(ws + L.redo);
   float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
-  void* part_o = ws + L.part_o;
+  uint16_t* part16 = reinterpret_cast<uint16_t*>(ws + L.part16);
+  float* part32 = reinterpret_cast<float*>(ws + L.part32);
 
   // In planner mode the split kernel plans for itself (no planner launch).
   mla::SplitParams sp{};
@@ -326,10 +324,10 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.num_splits = num_splits;
   sp.split_offset = split_offset;
   sp.work = work;
-  sp.redo = redo;
   sp.out = static_cast<uint16_t*>(out);
   sp.lse = lse;
-  sp.part_o = part_o;
+  sp.part16 = part16;
+  sp.part32 = part32;
   sp.part_lse = part_lse;
   sp.q_nope_sb = d->q_nope_sb;
   sp.q_nope_sh = d->q_nope_sh;
@@ -358,18 +356,14 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   // Timing (when enabled): each launch is timed from its dispatch packet.
   TimingSlot ts;
   hipEvent_t* ev = timing_slot(&ts) ? ts.ev : nullptr;
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), false, stream,
+  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), stream,
                              ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
-  // Work items whose main pass overflowed the P range are redone with their
-  // exact max; every other workgroup of this launch exits at once.
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), true, stream,
-                             ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)) != hipSuccess)
-    return fail(MLA_ERR_HIP, "redo launch: %s", hipGetErrorString(e));
 
   if (per_seq != 1) {
     mla::CombineParams cp{};
-    cp.part_o = part_o;
+    cp.part16 = part16;
+    cp.part32 = part32;
     cp.part_lse = part_lse;
     cp.split_offset = split_offset;
     cp.out = static_cast<uint16_t*>(out);
@@ -380,8 +374,8 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     cp.heads = d->heads;
     // Splits per sequence on average: forced, or at most max_work / B.
     const int mean_splits = per_seq > 0 ? per_seq : (max_work + d->batch - 1) / (d->batch > 0 ? d->batch : 1);
-    if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream, ev ? ev[4] : nullptr,
-                                 ev ? ev[5] : nullptr)) != hipSuccess)
+    if ((e = mla::launch_combine(cp, d->dtype, d->batch, mean_splits, stream, ev ? ev[2] : nullptr,
+                                 ev ? ev[3] : nullptr)) != hipSuccess)
       return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     if (ev) {
       std::lock_guard<std::mutex> lk(g_tmu);
@@ -398,13 +392,13 @@ int mla_timing_enable(int enable) {
   return ok();
 }
 
-int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t* calls) {
-  if (!split_ms || !rerun_ms || !combine_ms || !calls) return fail(MLA_ERR_INVALID_ARG, "NULL output");
+int mla_timing_read(float* split_ms, float* combine_ms, int32_t* calls) {
+  if (!split_ms || !combine_ms || !calls) return fail(MLA_ERR_INVALID_ARG, "NULL output");
   std::lock_guard<std::mutex> lk(g_tmu);
-  double acc[3] = {0, 0, 0};
+  double acc[2] = {0, 0};
   for (int i = 0; i < g_timed; ++i) {
     hipEvent_t* ev = &g_events[kEventsPerCall * (size_t)i];
-    const int launches = g_combined[i] ? 3 : 2;
+    const int launches = g_combined[i] ? 2 : 1;
     hipError_t e = hipEventSynchronize(ev[2 * launches - 1]);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
     for (int k = 0; k < launches; ++k) {
@@ -415,8 +409,7 @@ int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t
     }
   }
   *split_ms = (float)acc[0];
-  *rerun_ms = (float)acc[1];
-  *combine_ms = (float)acc[2];
+  *combine_ms = (float)acc[1];
   *calls = g_timed;
   g_timed = 0;
   return ok();

@@ -18,11 +18,11 @@ struct SplitParams {
   int32_t* num_splits;          // planner mode: written by workgroup 0 for the combine
   int32_t* split_offset;        // planner mode: [B + 1], written by workgroup 0
   int32_t* work;                // planner mode: work list (4 ints per item), written by workgroup 0
-  int32_t* redo;                // [max_work][head groups]: main pass overflowed, rerun with the exact max
   uint16_t* out;
   float* lse;
-  void* part_o;                 // [max_work, H, 512]: fp16 for fp16 inputs, else fp32
-  float* part_lse;              // [max_work, H], base 2
+  uint16_t* part16;             // [max_work, H, 512] fp16 normalised partial rows (every row)
+  float* part32;                // [max_work, H, 512] fp32 copies of rows with values beyond +-1
+  float* part_lse;              // [max_work, H], base 2; low mantissa bit set: the row has an fp32 copy
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
   int64_t out_sb, out_sh;
@@ -38,7 +38,8 @@ struct SplitParams {
 };
 
 struct CombineParams {
-  const void* part_o;           // fp16 for fp16 inputs, else fp32
+  const uint16_t* part16;       // [max_work, H, 512] fp16 partial rows
+  const float* part32;          // fp32 copies (rows whose lse has the low bit set)
   const float* part_lse;
   const int32_t* split_offset;  // planner mode
   uint16_t* out;
@@ -59,8 +60,8 @@ struct PlanParams {
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 // t0 / t1: events that time the launch from its dispatch packet, or null.
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
-                        hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream,
+                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // mean_splits: splits per sequence, on average (forced count, or the plan's
 // bound over the batch); from kCombineSplitkMin on, four waves share a head.
 constexpr int kCombineSplitkMin = 16;

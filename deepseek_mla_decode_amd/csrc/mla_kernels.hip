@@ -6,8 +6,7 @@
 //                    inside split_kernel, every wave for its own work item).
 //   * split_kernel   one workgroup per (work item, head group of 128 heads);
 //                    streams the work item's KV rows through LDS and runs the
-//                    base-2 online softmax with both products on MFMA.  Its
-//                    REDO instance reruns the items whose fixed max fell short.
+//                    base-2 online softmax with both products on MFMA.
 //   * combine_heads_kernel / combine_splitk_kernel merge the per-split
 //                    partials of sequences with s_b > 1: one wave per head for
 //                    few splits, four waves over the splits of a head for many.
@@ -164,6 +163,19 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Split partials: a row whose values all lie within [-kPart16Max,
+// kPart16Max] is kept in fp16 only; a larger one in fp32 too.  The choice
+// rides in the low mantissa bit of the row's base-2 lse (a change of one
+// ulp; -inf, the empty split, has it clear).
+constexpr float kPart16Max = 1.0f;
+__device__ __forceinline__ float lse_with_flag(float lse2, bool big) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, lse2) & ~1u) | (big ? 1u : 0u));
+}
+__device__ __forceinline__ bool lse_flag(float raw) { return (__builtin_bit_cast(uint32_t, raw) & 1u) != 0; }
+__device__ __forceinline__ float lse_value(float raw) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, raw) & ~1u);
+}
+
 // ---------------------------------------------------------------------------
 // LDS tile layout
 // ---------------------------------------------------------------------------
@@ -233,6 +245,12 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// max(a, |b|, |c|) in one VALU op (operand modifiers).
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // Split planner inside the split kernel
@@ -241,7 +259,7 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // plan_rule.h itself, on one wave with no barrier: the same integers as the
 // host twin and the stand-alone planner kernel.  This saves a kernel launch
 // per call.  Workgroup 0 publishes the plan (num_splits, split_offset, work)
-// for the rerun launch and the combine kernel.
+// for the combine kernel.
 
 // Sum and max over the 64 lanes: DPP within each row of 16 lanes (pairs,
 // quads, halves, rows), then the four row results through readlane.  Every
@@ -590,22 +608,34 @@ __device__ __forceinline__ void issue_part(const DmaCursor& c, const DmaTile& d,
 // P = 2^(c x - c m) and pack P as the B operand of P·V.  c = softmax_scale ·
 // log2(e) > 0, so the max of the raw scores is the max of the scaled ones.
 //
-// The reference max `m` does not change during the pass over the tiles
-// (changing it would mean rescaling the accumulator, which must never leave
-// the AGPRs).  The main pass takes m from the first tile, so P may exceed 1;
-// that is exact while P stays inside the range of the P·V operand type.  If
-// some tile's max passes m by more than the margin, the main pass writes no
-// output: it flags the work item and stores the exact max (`mx`, the max over
-// all tiles); the REDO launch then recomputes the work item with m = mx.
-template <int DT, bool REDO>
+// The reference max `m` is taken from the work item's first tile and then
+// changed only when a later tile's max passes it by more than kRescaleMargin
+// (log2 units): P = 2^(c x - c m) may exceed 1, which is exact while it stays
+// inside the range of the P·V operand type.  Step 5 leaves dn = c m - c
+// tmax (<= 0 when the tile's max is higher); raising m means scaling the
+// accumulator (all 256 AGPRs of the lane) and the running sums by alpha =
+// 2^dn, which the loop does in a rarely taken branch right after step 5,
+// before this tile's exponentials and sums.  Only nmc = -c m is kept.
+//
+// Two running sums of P: `lsum` of the fp32 values (it gives the split's
+// log-sum-exp, hence the weights between splits) and, for fp16, `lsr` of the
+// values as rounded for the P·V product.  The split's output is normalised by
+// lsr, so that it is exactly a convex combination of value rows under the
+// weights actually multiplied: the rounding of a dominant P then cancels.
+// bf16 keeps P as hi + lo (relative error 2^-17), so lsum serves both.
+template <int DT>
+constexpr float kRescaleMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
+
+template <int DT>
 struct Softmax {
   float x[16];
   float t0, t1, t2, t3, t4, tmax;
+  float dn;             // step 5: c m - c tmax (0 on the first tile)
   u32x4 pk[2], pl[2];   // P packed (bf16: high part in pk, low part in pl)
 
   // Step `s` (0..22).  `first`: this is the work item's first tile, which
-  // fixes m; only nmc = -c m is kept.  mx tracks the max over all tiles.
-  __device__ __forceinline__ void step(int s, bool first, float c, float& nmc, float& mx, float& lsum) {
+  // fixes m.
+  __device__ __forceinline__ void step(int s, bool first, float c, float& nmc, float& lsum, float& lsr) {
     if (s == 0) { t0 = max3(x[0], x[1], x[2]); t1 = max3(x[3], x[4], x[5]); }
     if (s == 1) { t2 = max3(x[6], x[7], x[8]); t3 = max3(x[9], x[10], x[11]); }
     if (s == 2) { t4 = max3(x[12], x[13], x[14]); t0 = max3(t0, t1, x[15]); }
@@ -616,11 +646,15 @@ struct Softmax {
       tmax = max3(a, b, b);
     }
     if (s == 5) {
-      mx = max3(mx, tmax, tmax);
-      // A query row with no visible row in the first tile (possible in a tail
-      // split) has tmax = -inf: it uses 0 as the max, so that P = 2^-inf = 0
-      // rather than 2^(-inf + inf).
-      if (!REDO && first) nmc = tmax == -__builtin_inff() ? 0.f : -(tmax * c);
+      if (first) {
+        // A query row with no visible row in the first tile (possible in a
+        // tail split) has tmax = -inf: it uses 0 as the max, so that P =
+        // 2^-inf = 0 rather than 2^(-inf + inf).
+        nmc = tmax == -__builtin_inff() ? 0.f : -(tmax * c);
+        dn = 0.f;
+      } else {
+        dn = __builtin_fmaf(tmax, -c, -nmc);   // -inf max: +inf, no rescale
+      }
     }
     if (s >= 6 && s < 22) {
       const int e = s - 6;
@@ -632,7 +666,10 @@ struct Softmax {
       const float a = x[2 * j], bb = x[2 * j + 1];
       const uint32_t w = pack2<DT>(a, bb);
       pk[j >> 2][j & 3] = w;
-      if constexpr (DT == MLA_DTYPE_BF16) {
+      if constexpr (DT == MLA_DTYPE_F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        lsr = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), (h2){(_Float16)1.0f, (_Float16)1.0f}, lsr, false);
+      } else {
         const float ah = __builtin_bit_cast(float, w << 16);
         const float bh = __builtin_bit_cast(float, w & 0xFFFF0000u);
         pl[j >> 2][j & 3] = pack2<DT>(a - ah, bb - bh);
@@ -642,9 +679,6 @@ struct Softmax {
 };
 constexpr int kSoftmaxSteps = 23;
 
-// REDO = false: the main pass.  REDO = true: the second launch, which only
-// reruns work items whose main pass flagged an overflow.
-//
 // Schedule (one wave, work item of n tiles; tile t in LDS slot t % 4):
 //   prologue   DMA tiles 0, 1, 2; wait for tile 0; barrier
 //   step t     A: the 36 score MFMAs of tile t, with the softmax of tile t-1
@@ -658,7 +692,7 @@ constexpr int kSoftmaxSteps = 23;
 //   drain      softmax of tile n-1 (masked), P·V of tile n-1.
 // Two tiles stay in flight, one barrier per tile; only the last tile can be
 // partial, so masking is confined to the drain.
-template <int DT, bool PAGED, bool REDO>
+template <int DT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kTileBytes + kQLdsBytes];
@@ -671,7 +705,7 @@ void split_kernel(SplitParams p) {
   // so that the splits of a sequence share one L2 for their queries, and the
   // head groups of a work item its cache rows.
   //
-  // With several query tokens (main pass) the workgroups come in two kinds,
+  // With several query tokens the workgroups come in two kinds,
   // the full-length prefix splits and the one-tile tails (work items below
   // tail * B, see plan_item); each XCD gets an even share of each kind, the
   // prefix splits first, so that the two head groups of a split start
@@ -683,7 +717,7 @@ void split_kernel(SplitParams p) {
     const int total = gridDim.x * ng;
     const int flat = blockIdx.x + blockIdx.y * gridDim.x;
     const int xcd = flat & (kXcds - 1), idx = flat / kXcds;
-    const int nt = REDO ? 0 : tail_splits(p.seqlen_q) * p.batch * ng;   // tail workgroups
+    const int nt = tail_splits(p.seqlen_q) * p.batch * ng;   // tail workgroups
     const int nb = total - nt;                                         // the others
     // Workgroups of each kind before XCD x, and on XCD x.
     auto before = [&](int n, int x) { return x * (n / kXcds) + min(x, n % kXcds); };
@@ -703,23 +737,16 @@ void split_kernel(SplitParams p) {
   const int g = lane >> 5;
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
-  // Rerun flags, one per (split slot, head group).  The main pass writes the
-  // flag of every split it runs (and of its workgroups past the end of the
-  // plan); the rerun launch, one workgroup per split slot, leaves at once
-  // when it is 0.
-  int32_t* redo_flag = p.redo + (wi * (int)gridDim.y + hg);
-  if (REDO && *redo_flag == 0) return;
-
   // ---- work item (uniform) -------------------------------------------------
   // k: the split's index within its sequence; with several query tokens the
   // last two splits are the tails, whose rows are masked per query row.
-  // split_slot (sequence-major) indexes the partials and rerun flags; in the
-  // main pass with tails, work items come tails first (see plan_item).
+  // split_slot (sequence-major) indexes the partials; with tails, work items
+  // come tails first (see plan_item).
   int b, k, r0, r1, s_b, split_slot = wi;
   if (p.num_split > 0) {
     s_b = p.num_split;
     const int tl = tail_splits(p.seqlen_q), pre = s_b - tl;
-    if (!REDO && tl > 0) {
+    if (tl > 0) {
       if (wi < tl * p.batch) {
         b = wi / tl;
         k = pre + wi % tl;
@@ -733,25 +760,15 @@ void split_kernel(SplitParams p) {
       k = wi - b * s_b;
     }
     seq_split_range(clamp_len(p.seqlens[b], p.row_cap), p.seqlen_q, pre, k, &r0, &r1);
-  } else if (!REDO) {
+  } else {
     const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
-    if (!it.valid) {   // past the end of the plan
-      if (threadIdx.x == 0) *redo_flag = 0;
-      return;
-    }
+    if (!it.valid) return;   // past the end of the plan
     b = it.b;
     k = it.k;
     r0 = it.r0;
     r1 = it.r1;
     s_b = it.s_b;
     split_slot = it.slot;
-  } else {
-    // The plan the main pass published (the flag was set, so wi is in it).
-    b = p.work[4 * wi + 0];
-    k = p.work[4 * wi + 1];
-    r0 = p.work[4 * wi + 2];
-    r1 = p.work[4 * wi + 3];
-    s_b = p.split_offset[b + 1] - p.split_offset[b];
   }
   // Tail splits (the last two with several query tokens): query token t sees
   // rows j < L - (seqlen_q - 1 - t) = tail_lim + t.  Other splits: no limit.
@@ -760,7 +777,6 @@ void split_kernel(SplitParams p) {
     tail_lim = clamp_len(p.seqlens[b], p.row_cap) - (p.seqlen_q - 1);
   tail_lim = __builtin_amdgcn_readfirstlane(tail_lim);
   split_slot = __builtin_amdgcn_readfirstlane(split_slot);
-  redo_flag = p.redo + (split_slot * (int)gridDim.y + hg);
   b = __builtin_amdgcn_readfirstlane(b);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
@@ -823,23 +839,17 @@ void split_kernel(SplitParams p) {
   // lse = -inf (or a zero partial, lse = -inf) and leaves before the
   // accumulator exists, so that it has a single definition path.
   if (n_tiles == 0) {
-    if (!REDO && threadIdx.x == 0) *redo_flag = 0;
-    if (REDO || !head_ok) return;
+    if (!head_ok) return;
     if (s_b == 1) {
       uint16_t* o = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 4 * g;
 #pragma unroll
       for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
       if (g == 0) p.lse[(int64_t)b * p.heads + h] = -__builtin_inff();
-    } else if constexpr (DT == MLA_DTYPE_F16) {
-      uint16_t* o = static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
+    } else {
+      uint16_t* o = p.part16 + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
 #pragma unroll
       for (int k = 0; k < 64; ++k) *reinterpret_cast<u32x2*>(o + 8 * k) = u32x2{0u, 0u};
-      if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();
-    } else {
-      float* o = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h) * 512 + 4 * g;
-#pragma unroll
-      for (int k = 0; k < 64; ++k) *reinterpret_cast<f32x4*>(o + 8 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();
+      if (g == 0) p.part_lse[(int64_t)split_slot * p.heads + h] = -__builtin_inff();   // low bit 0: fp16 row
     }
     return;
   }
@@ -886,7 +896,7 @@ void split_kernel(SplitParams p) {
   // A wave whose 32 heads all lie past the last head (few heads per group)
   // computes nothing: it only issues its share of every tile's loads and
   // passes the same barriers as the other waves (prologue; one per step; the
-  // two around the overflow words), then leaves.  Wave 0 always has heads.
+  // one before the epilogue), then leaves.  Wave 0 always has heads.
   if (h0 >= p.heads) {
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
@@ -914,29 +924,17 @@ void split_kernel(SplitParams p) {
       barrier();
     }
     wait_cnt<0, 15>();
-    if (!REDO) {
-      int* flags = reinterpret_cast<int*>(lds_raw);
-      __syncthreads();
-      if (lane == 0) flags[wave] = 0;
-      __syncthreads();
-    } else {
-      __syncthreads();   // the other waves' barrier before their epilogue
-    }
+    __syncthreads();   // the computing waves' barrier before their epilogue
     return;
   }
 
   f32x16 acc[16];
 #pragma unroll
   for (int vb = 0; vb < 16; ++vb) acc[vb] = f32x16{};
-  // Reference max m (raw-score units): the REDO launch reads it, the main
-  // pass takes it from the first tile.
+  // nmc = -c m for the reference max m, set from the first tile (Softmax).
   float nmc = 0.f;
-  if (REDO) {
-    const float m = p.part_lse[(int64_t)split_slot * p.heads + h];
-    nmc = m == -__builtin_inff() ? 0.f : -(m * c);
-  }
-  float mx = -__builtin_inff();   // running max of all tiles seen (raw)
-  float lsum = 0.f;               // this lane's share of the sum of P
+  float lsum = 0.f;   // this lane's share of the sum of P (fp32 values)
+  float lsr = 0.f;    // fp16: the same of the rounded values
 
   {
     // ---- prologue ----------------------------------------------------------
@@ -965,7 +963,7 @@ void split_kernel(SplitParams p) {
     u32x4 kb[kKB], vbuf[kVB], qb[4];
     uint32_t kq[8], vw[4];
     f32x16 sA, sB;
-    Softmax<DT, REDO> sm;
+    Softmax<DT> sm;
 
     // Score-operand bases of a tile, then its first kKA K reads.
     auto k_head = [&](const lds_char* tile) __attribute__((always_inline)) {
@@ -995,6 +993,38 @@ void split_kernel(SplitParams p) {
       // Half r = 1 is half 0 with bit 5 flipped (the tile base is 1 KiB aligned).
       return lds_get_tr(lds_at(vw[vb & 3]), imm, lds_at(xor_imm<32>(vw[vb & 3])), imm + 8192);
     };
+    // A tile whose max passed the reference by more than the margin (Softmax
+    // step 5 leaves dn < -margin): raise the reference to that max and scale
+    // the accumulator and the running sums by alpha = 2^dn, before this
+    // tile's exponentials.  The accumulator then holds the tiles before it;
+    // their last P·V MFMAs are complete (the padding waits them out anyway).
+    // Rare (never on N(0,1) inputs), so a wave-uniform branch: scaling the
+    // 256 AGPRs takes some 800 instructions.  One asm statement per register
+    // (read, multiply, write back): a vector multiply of the accumulator
+    // tiles lets the register allocator move them to VGPRs and spill the
+    // queries inside the tile loop.
+    auto rescale = [&]() __attribute__((always_inline)) {
+      if (__builtin_amdgcn_ballot_w64(sm.dn < -kRescaleMargin<DT>) != 0) {
+        const float dz = sm.dn < -kRescaleMargin<DT> ? sm.dn : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(dz);
+        nmc += dz;
+        lsum *= alpha;
+        lsr *= alpha;
+        nops_after_mfma(acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(acc[i][j]), "=&v"(tmp)
+                         : "v"(alpha));
+          }
+        }
+        nops_after_mfma(acc);
+      }
+    };
+
     // Score MFMAs of one tile into `sc`; with WITH_SM, the softmax of the
     // previous tile runs between them and the first kVA V reads of the
     // previous tile are issued at the end.
@@ -1006,20 +1036,29 @@ void split_kernel(SplitParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sm.x[e] = prev[e];
       }
-#pragma unroll
-      for (int s = 0; s < 36; ++s) {
+      auto a_step = [&](int s) __attribute__((always_inline)) {
         if (s == 0) mfma_v<DT, true>(sc, kb[0], qreg[0]);
         else mfma_v<DT, false>(sc, kb[s % kKB], q_op(s));
         if (s + kKA < 36) kb[(s + kKA) % kKB] = k_read(tile, s + kKA);
         if (s + kKA >= kQRegSteps && s + kKA < 36)
           qb[s + kKA - kQRegSteps] = lds_get16(lds_at(xor_add(qwave, 0u, lane16)), (s + kKA - kQRegSteps) * 4096);
         if (with_sm) {
-          if (s < kSoftmaxSteps) sm.step(s, first_prev, c, nmc, mx, lsum);
+          if (s < kSoftmaxSteps) sm.step(s, first_prev, c, nmc, lsum, lsr);
           if (s == 30) v_bases(vtile);
           if (s >= 36 - kVA) vbuf[s - (36 - kVA)] = v_read(s - (36 - kVA));
         }
         fence();
+      };
+      // The rescale branch sits between softmax steps 5 and 6, outside the
+      // unrolled loops (inside one, it stops the unrolling).
+#pragma unroll
+      for (int s = 0; s < 6; ++s) a_step(s);
+      if (with_sm) {
+        rescale();
+        fence();
       }
+#pragma unroll
+      for (int s = 6; s < 36; ++s) a_step(s);
     };
     // P·V MFMAs of one tile, operands [i0, i1), V reads kVA ahead.  With
     // WITH_DMA, this wave's 9 loads of tile dma_t (page dma_pg) go one every
@@ -1071,7 +1110,10 @@ void split_kernel(SplitParams p) {
     // ---- steps 1 .. n-1, two per trip so the score tiles alternate ---------
     // Step t issues tile t+2 into the slot of tile t-2.
     // Every step loads a tile and passes a barrier, also the last ones (see
-    // cursor_next), so that the loop has no branch but its back edge.
+    // cursor_next), so that the loop has no branch but its back edge.  (Step
+    // 1, the softmax of tile 0 that fixes the reference max, stays in the
+    // loop: run before it, it made the register allocator move accumulator
+    // tiles between the two copies of the step.)
     auto step = [&](int t, f32x16& cur, f32x16& prev) __attribute__((always_inline)) {
       phase_a(slot(t), cur, prev, true, t == 1, slot(t - 1));
       nops_before_mfma<DT>(sm.pk, sm.pl);
@@ -1079,10 +1121,15 @@ void split_kernel(SplitParams p) {
       pg_next = advance(t);
       pv_range(32 - kVA, 32, false, 0, 0);
     };
+    // The padding at the end of a trip: with the rescale branch in the loop,
+    // the register allocator may swap accumulator tiles on the loop's exit
+    // edge, right behind the last P·V MFMA; the wait states cost nothing
+    // while that MFMA still occupies the matrix core.
     int t = 1;
     for (; t + 1 < n_tiles; t += 2) {
       step(t, sB, sA);
       step(t + 1, sA, sB);
+      nops_after_mfma(acc);
     }
     if (t < n_tiles) step(t, sB, sA);
 
@@ -1102,7 +1149,10 @@ void split_kernel(SplitParams p) {
         sm.x[e] = tile_base + n < lim ? last[e] : -__builtin_inff();
       }
 #pragma unroll
-      for (int s = 0; s < kSoftmaxSteps; ++s) sm.step(s, n_tiles == 1, c, nmc, mx, lsum);
+      for (int s = 0; s < kSoftmaxSteps; ++s) {
+        sm.step(s, n_tiles == 1, c, nmc, lsum, lsr);
+        if (s == 5) rescale();
+      }
       v_bases(slot(n_tiles - 1));
 #pragma unroll
       for (int i = 0; i < kVA; ++i) vbuf[i] = v_read(i);
@@ -1121,94 +1171,102 @@ void split_kernel(SplitParams p) {
   const int g_t = lane_t >> 5;
   const int h_t = h0 + (lane_t & 31);
   const bool head_ok_t = h_t < p.heads;
-  if (!REDO) {
-    // Overflow: some tile's max passed m by more than the margin (log2
-    // units), i.e. P left the exact range of the operand type.
-    constexpr float kOverflowMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
-    const bool ovf = __any(__builtin_fmaf(mx, c, nmc) > kOverflowMargin);
-    // Agree on the flag through the first words of the tile ring, which no
-    // wave reads any more once all have passed the first barrier.
-    int* flags = reinterpret_cast<int*>(lds_raw);
-    __syncthreads();
-    if (lane_t == 0) flags[wave] = ovf ? 1 : 0;
-    __syncthreads();
-    const bool overflow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
-    if (overflow) {
-      if (wave == 0 && lane_t == 0) *redo_flag = 1;
-      if (head_ok_t && g_t == 0) p.part_lse[(int64_t)split_slot * p.heads + h_t] = mx;
-      return;
-    }
-    if (wave == 0 && lane_t == 0) *redo_flag = 0;
-  }
-
   // ---- epilogue: normalise; write final output or the split partial --------
+  // lse from the fp32 sum; the output normalised by the sum of the values the
+  // P·V product used (fp16: the rounded sum; see Softmax).
   const float ltot = halves_sum(lsum);
+  const float lnorm = DT == MLA_DTYPE_F16 ? halves_sum(lsr) : ltot;
   const bool nonempty = ltot > 0.f;
-  const float inv = nonempty ? 1.f / ltot : 0.f;
+  const float inv = nonempty ? 1.f / lnorm : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) - nmc : -__builtin_inff();
-  if (head_ok_t && g_t == 0) {
-    if (s_b == 1) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
-    else p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse2;
-  }
+  if (s_b == 1 && head_ok_t && g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
   // The rows leave through LDS: each wave stages its 32 head rows in a
-  // region of its own (past the overflow words), then writes one whole row
-  // (1 KiB, 16 bytes per lane) per store instruction.  Straight from the
-  // accumulator layout, a store would cover 16-byte pieces of 32 rows.
-  // Staged 16-byte chunk c of row r sits at chunk c ^ r: the accumulator
-  // writes (32 rows) and the row reads (64 chunks of one row) are both free
-  // of bank conflicts.  Every wave has finished with the tile ring: the main
-  // pass passed the two barriers around the overflow words; the rerun passes
-  // this one (idle waves pass it too).
-  if (REDO) __syncthreads();
-  lds_char* stage = lds + 256 + wave * 32768;
+  // region of its own, then writes one whole row (1 KiB, 16 bytes per lane)
+  // per store instruction.  Straight from the accumulator layout, a store
+  // would cover 16-byte pieces of 32 rows.  Staged 16-byte chunk c of row r
+  // sits at chunk c ^ r: the accumulator writes (32 rows) and the row reads
+  // (64 chunks of one row) are both free of bank conflicts.  The barrier
+  // makes sure that every wave has finished reading the tile ring (idle
+  // waves pass it too).
+  __syncthreads();
+  lds_char* stage = lds + wave * 32768;
   const int hl_t = lane_t & 31;
   auto stage_at = [&](int row, int chunk) __attribute__((always_inline)) {
     return stage + row * 1024 + ((chunk ^ row) << 4);
   };
-  if (s_b == 1 || DT == MLA_DTYPE_F16) {
-    // 16-bit rows (the output, or the fp16 partial: the output's own
-    // precision, one more rounding of at most 2^-12 of |O_k| before the
-    // weighted average): 512 values = 64 chunks of 8; this lane holds
-    // values 8 q + 4 g .. + 3 of chunk 4 vb + q.
+  // 16-bit rows, 512 values = 64 chunks of 8; this lane holds values
+  // 8 q + 4 g .. + 3 of chunk 4 vb + q.  ODT: the output's type, or fp16 for
+  // a partial, whose largest |value| (this lane's half row) it returns.
+  auto stage16 = [&](auto odt, auto partial) __attribute__((always_inline)) -> float {
+    constexpr int ODT = decltype(odt)::value;
+    constexpr bool PART = decltype(partial)::value;
+    float rmax = 0.f;
 #pragma unroll
     for (int vb = 0; vb < 16; ++vb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        const float a0 = acc[vb][4 * q + 0] * inv, a1 = acc[vb][4 * q + 1] * inv;
+        const float a2 = acc[vb][4 * q + 2] * inv, a3 = acc[vb][4 * q + 3] * inv;
+        if (PART) {
+          rmax = max3_abs(rmax, a0, a1);
+          rmax = max3_abs(rmax, a2, a3);
+        }
         u32x2 w;
-        w.x = pack2<DT>(acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv);
-        w.y = pack2<DT>(acc[vb][4 * q + 2] * inv, acc[vb][4 * q + 3] * inv);
+        w.x = pack2<ODT>(a0, a1);
+        w.y = pack2<ODT>(a2, a3);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage_at(hl_t, 4 * vb + q) + 8 * g_t) = w;
       }
     }
+    return rmax;
+  };
+  // skip_rows: bit r set leaves row r out (a partial row kept in fp32).
+  auto store16 = [&](uint16_t* row0, int64_t row_stride, uint32_t skip_rows) __attribute__((always_inline)) {
 #pragma unroll 4
     for (int r = 0; r < 32; ++r) {
       if (h0 + r >= p.heads) break;
-      uint16_t* row = s_b == 1 ? p.out + (int64_t)b * p.out_sb + (int64_t)(h0 + r) * p.out_sh
-                               : static_cast<uint16_t*>(p.part_o) + ((int64_t)split_slot * p.heads + h0 + r) * 512;
+      if ((skip_rows >> r) & 1u) continue;
       const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage_at(r, lane_t));
-      *reinterpret_cast<u32x4*>(row + 8 * lane_t) = v;
+      *reinterpret_cast<u32x4*>(row0 + r * row_stride + 8 * lane_t) = v;
     }
-  } else {
-    // fp32 partial rows (bf16 inputs), in two halves of 256 values = 64
-    // chunks of 4; this lane holds chunk 8 (vb % 8) + 2 q + g.
+  };
+  if (s_b == 1) {
+    stage16(std::integral_constant<int, DT>{}, std::false_type{});
+    store16(p.out + (int64_t)b * p.out_sb + (int64_t)h0 * p.out_sh, p.out_sh, 0u);
+    return;
+  }
+  // Split partial.  A row whose values all lie within +-kPart16Max goes out
+  // in fp16; a wider one in fp32 only (its fp16 slot is left as it was), and
+  // the low bit of its lse says so.  An fp16 row then adds at most 2^-12
+  // (half an ulp below 1) per value to the combined output, whatever the
+  // weights; a 16-bit copy of larger values would add 2^-12 |O_k|, which
+  // exceeds the absolute tolerance where large value rows of two splits
+  // cancel.
+  const float rmax = halves_max(stage16(std::integral_constant<int, MLA_DTYPE_F16>{}, std::true_type{}));
+  const bool big = rmax > kPart16Max;
+  if (head_ok_t && g_t == 0)
+    p.part_lse[(int64_t)split_slot * p.heads + h_t] = lse_with_flag(lse2, big);
+  const uint32_t bigrows = (uint32_t)__builtin_amdgcn_ballot_w64(big);   // bit r: head h0 + r
+  store16(p.part16 + ((int64_t)split_slot * p.heads + h0) * 512, 512, bigrows);
+  if (bigrows == 0) return;
+  // fp32 rows of the large ones, in two halves of 256 values = 64 chunks of
+  // 4; this lane holds chunk 8 (vb % 8) + 2 q + g.
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int vb = 8 * half; vb < 8 * half + 8; ++vb) {
+    for (int vb = 8 * half; vb < 8 * half + 8; ++vb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
-                           acc[vb][4 * q + 3] * inv};
-          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage_at(hl_t, 8 * (vb & 7) + 2 * q + g_t)) = w;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
+                         acc[vb][4 * q + 3] * inv};
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage_at(hl_t, 8 * (vb & 7) + 2 * q + g_t)) = w;
       }
-#pragma unroll 4
-      for (int r = 0; r < 32; ++r) {
-        if (h0 + r >= p.heads) break;
-        float* row = static_cast<float*>(p.part_o) + ((int64_t)split_slot * p.heads + h0 + r) * 512 + 256 * half;
-        const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(stage_at(r, lane_t));
-        *reinterpret_cast<f32x4*>(row + 4 * lane_t) = v;
-      }
+    }
+    for (int r = 0; r < 32; ++r) {
+      if (h0 + r >= p.heads) break;
+      if (((bigrows >> r) & 1u) == 0) continue;
+      float* row = p.part32 + ((int64_t)split_slot * p.heads + h0 + r) * 512 + 256 * half;
+      const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(stage_at(r, lane_t));
+      *reinterpret_cast<f32x4*>(row + 4 * lane_t) = v;
     }
   }
 }
@@ -1245,19 +1303,53 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
-// Eight values of a partial row (element offset e): fp16 partials (fp16
-// inputs) in one 16-byte read, fp32 partials in two.
-template <int DT>
-__device__ __forceinline__ void load_part8(const void* part_o, int64_t e, f32x4& v0, f32x4& v1) {
-  if constexpr (DT == MLA_DTYPE_F16) {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(part_o) + e);
-    v0 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.x, w.y}), f32x4);
-    v1 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.z, w.w}), f32x4);
-  } else {
-    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(part_o) + e);
-    v0 = src[0];
-    v1 = src[1];
+// Eight values (element offset e) of a partial row: fp16 rows in one 16-byte
+// read, fp32 rows in two.
+__device__ __forceinline__ void load_part16x8(const uint16_t* part16, int64_t e, f32x4& v0, f32x4& v1) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = *reinterpret_cast<const u32x4*>(part16 + e);
+  v0 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.x, w.y}), f32x4);
+  v1 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.z, w.w}), f32x4);
+}
+__device__ __forceinline__ void load_part32x8(const float* part32, int64_t e, f32x4& v0, f32x4& v1) {
+  const f32x4* src = reinterpret_cast<const f32x4*>(part32 + e);
+  v0 = src[0];
+  v1 = src[1];
+}
+
+// a += w v for an fp16 partial row, or nothing when `skip`: a wide split,
+// whose fp16 slot holds stale bits (possibly NaN), or a batch entry past the
+// last split, which re-read the last one (possibly wide).  The product is
+// selected away rather than weighted by 0, since 0 * NaN is NaN.
+__device__ __forceinline__ void add_fp16_part(f32x4& a0, f32x4& a1, float w, f32x4 v0, f32x4 v1, bool skip) {
+  const f32x4 t0 = w * v0, t1 = w * v1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0[i] += skip ? 0.f : t0[i];
+    a1[i] += skip ? 0.f : t1[i];
+  }
+}
+
+// a += w(u) v_u for the wide splits u of a batch of U (bit u of `wide`):
+// their fp32 rows at O + first + u * step, all read before any is added;
+// the other slots of the batch re-read the first wide row (a cache hit) and
+// add it with weight 0.  v0 / v1 are the batch's row registers, free by now.
+template <int U, typename WeightOf>
+__device__ __forceinline__ void add_fp32_parts(f32x4& a0, f32x4& a1, const float* part32, int64_t O, int64_t step,
+                                               int64_t first, uint32_t wide, f32x4 (&v0)[U], f32x4 (&v1)[U],
+                                               WeightOf weight_of) {
+  if (wide == 0) return;
+  const int f = __builtin_ctz(wide);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int uu = ((wide >> u) & 1u) ? u : f;
+    load_part32x8(part32, O + first + (int64_t)uu * step, v0[u], v1[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float w = ((wide >> u) & 1u) ? weight_of(u) : 0.f;
+    a0 += w * v0[u];
+    a1 += w * v1[u];
   }
 }
 
@@ -1276,30 +1368,30 @@ __device__ __forceinline__ void combine_range(const CombineParams& p, int b, int
 }
 
 // Final base-2 lse of a head from the split lse values held two per lane
-// (l0 of split lane, l1 of split lane + 64; -inf past the splits) plus any
-// splits beyond the first 128, and this lane's weight for split `lane`.  A head
-// whose splits are all empty gets total = -inf and weight 0 everywhere
-// (output 0, lse -inf), without a branch, so that the partial-row reads
-// already in flight stay in flight.
+// (l0 of split lane, l1 of split lane + 64; -inf past the splits; format
+// bits already cleared) plus any splits beyond the first 128, and this lane's
+// weight for split `lane`.  A head whose splits are all empty gets total =
+// -inf and weight 0 everywhere (output 0, lse -inf), without a branch, so
+// that the partial-row reads already in flight stay in flight.
 struct CombineWeights {
   float total, w_own;
 };
 __device__ __forceinline__ CombineWeights combine_weights(float l0, float l1, const float* L, int heads, int s,
                                                           int lane) {
   float mx = fmaxf(l0, l1);
-  for (int k = lane + 128; k < s; k += 64) mx = fmaxf(mx, L[(int64_t)k * heads]);
+  for (int k = lane + 128; k < s; k += 64) mx = fmaxf(mx, lse_value(L[(int64_t)k * heads]));
   mx = wave_max(mx);
   const float ref = mx == -__builtin_inff() ? 0.f : mx;
   float se = __builtin_amdgcn_exp2f(l0 - ref) + __builtin_amdgcn_exp2f(l1 - ref);   // 0 past s
-  for (int k = lane + 128; k < s; k += 64) se += __builtin_amdgcn_exp2f(L[(int64_t)k * heads] - ref);
+  for (int k = lane + 128; k < s; k += 64) se += __builtin_amdgcn_exp2f(lse_value(L[(int64_t)k * heads]) - ref);
   se = wave_sum(se);
   const float total = __log2f(se) + ref;   // -inf when every split is empty
   const float w_own = se > 0.f ? __builtin_amdgcn_exp2f(l0 - total) : 0.f;
   return {total, w_own};
 }
 
-// lse of split k = lane + 64 j as held by the lane (-inf past s), read without
-// a branch: lanes past s re-read split s - 1.
+// lse of split k = lane + 64 j as held by the lane, with its format bit
+// (-inf past s), read without a branch: lanes past s re-read split s - 1.
 __device__ __forceinline__ float lane_lse(const float* L, int heads, int s, int k) {
   const float l = L[(int64_t)(k < s ? k : s - 1) * heads];
   return k < s ? l : -__builtin_inff();
@@ -1308,6 +1400,9 @@ __device__ __forceinline__ float lane_lse(const float* L, int heads, int s, int 
 // One wave merges the s splits of head h of sequence b; lane l owns output
 // columns 8 l .. 8 l + 7.  S = s when s is 2..kCombineUnroll (every read of
 // the partial rows issued before the first wait), S = 0 for any larger count.
+// The fp16 rows are read together with the lse values and accumulated; a
+// split whose lse carries the format bit (its fp16 slot holds stale data,
+// selected away) has its fp32 row read and added afterwards.
 template <int DT, int S>
 __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int h, int lane, int s_rt, int base) {
   constexpr int U = S ? S : kCombineUnroll;
@@ -1317,20 +1412,22 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
   const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
   // Lane k holds the lse of split k (and k + 64).  The first U partial rows
   // are read in the same round trip: they do not depend on the weights.
-  const float l0 = lane_lse(L, p.heads, s, lane);
-  const float l1 = S ? -__builtin_inff() : lane_lse(L, p.heads, s, lane + 64);
+  const float r0 = lane_lse(L, p.heads, s, lane);
+  const float r1 = S ? -__builtin_inff() : lane_lse(L, p.heads, s, lane + 64);
   f32x4 v0[U], v1[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_part8<DT>(p.part_o, O + (int64_t)u * stride, v0[u], v1[u]);
+  for (int u = 0; u < U; ++u) load_part16x8(p.part16, O + (int64_t)u * stride, v0[u], v1[u]);
   __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
-  const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
+  const uint64_t wide = __builtin_amdgcn_ballot_w64(lse_flag(r0));   // bit k: split k has an fp32 row
+  const CombineWeights cw = combine_weights(lse_value(r0), lse_value(r1), L, p.heads, s, lane);
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const float w = lane_f32(cw.w_own, u);   // split u's weight, held by lane u
-    a0 += w * v0[u];
-    a1 += w * v1[u];
+    add_fp16_part(a0, a1, w, v0[u], v1[u], (wide >> u) & 1ull);
   }
+  add_fp32_parts<U>(a0, a1, p.part32, O, stride, 0, (uint32_t)(wide & ((1ull << U) - 1ull)), v0, v1,
+                    [&](int u) __attribute__((always_inline)) { return lane_f32(cw.w_own, u); });
   if constexpr (S == 0) {
     // s > U: further batches of U; indices past s re-read split s - 1 with weight 0.
     const bool any = cw.total != -__builtin_inff();
@@ -1339,15 +1436,20 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = k0 + u < s ? k0 + u : s - 1;
-        load_part8<DT>(p.part_o, O + (int64_t)k * stride, v0[u], v1[u]);
+        load_part16x8(p.part16, O + (int64_t)k * stride, v0[u], v1[u]);
         lk[u] = L[(int64_t)k * p.heads];
       }
+      float wk[U];
+      uint32_t wm = 0;   // lk[u] is the same in every lane
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float w = any && k0 + u < s ? __builtin_amdgcn_exp2f(lk[u] - cw.total) : 0.f;
-        a0 += w * v0[u];
-        a1 += w * v1[u];
+        wk[u] = any && k0 + u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
+        const bool wd = k0 + u < s && lse_flag(lk[u]);
+        wm |= wd ? 1u << u : 0u;
+        add_fp16_part(a0, a1, wk[u], v0[u], v1[u], wd || k0 + u >= s);
       }
+      add_fp32_parts<U>(a0, a1, p.part32, O, stride, (int64_t)k0 * stride, wm, v0, v1,
+                        [&](int u) __attribute__((always_inline)) { return wk[u]; });
     }
   }
   u32x4 r;
@@ -1399,9 +1501,10 @@ __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
 }
 
 // Wave w accumulates splits w, w + 4, ... in batches of kSplitkBatch (8
-// output values per lane; a batch's partial rows and lse values are read
-// together, the first batch before the final lse is known); the four sums meet
-// in LDS, and wave w writes output columns 128 w .. 128 w + 127.
+// output values per lane; a batch's fp16 partial rows and lse values are
+// read together, the first batch before the final lse is known; the fp32
+// rows of the splits whose lse carries the format bit are added after); the four sums
+// meet in LDS, and wave w writes output columns 128 w .. 128 w + 127.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   __shared__ f32x4 red[4][2][64];   // [wave][half][lane]: 8 values per lane
@@ -1416,7 +1519,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
   const int64_t stride = (int64_t)p.heads * 512;   // elements between consecutive splits
   const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
-  const float l0 = lane_lse(L, p.heads, s, lane), l1 = lane_lse(L, p.heads, s, lane + 64);
+  const float l0 = lse_value(lane_lse(L, p.heads, s, lane)), l1 = lse_value(lane_lse(L, p.heads, s, lane + 64));
   // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
   // s re-read split s - 1, which then gets weight 0.
   f32x4 v0[U], v1[U];
@@ -1425,10 +1528,11 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
-      load_part8<DT>(p.part_o, O + (int64_t)k * stride, v0[u], v1[u]);
+      load_part16x8(p.part16, O + (int64_t)k * stride, v0[u], v1[u]);
       lk[u] = L[(int64_t)k * p.heads];
     }
   };
+
   load_batch(wave);
   __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
   const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
@@ -1436,12 +1540,18 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = wave;;) {
+    float wk[U];
+    uint32_t wm = 0;   // lk[u] is the same in every lane
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lk[u] - cw.total) : 0.f;
-      a0 += w * v0[u];
-      a1 += w * v1[u];
+      wk[u] = any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
+      const bool wd = k0 + 4 * u < s && lse_flag(lk[u]);
+      wm |= wd ? 1u << u : 0u;
+      add_fp16_part(a0, a1, wk[u], v0[u], v1[u], wd || k0 + 4 * u >= s);
     }
+    // Splits k0 + 4 u: the fp32 rows of the wide ones (stride 4 splits).
+    add_fp32_parts<U>(a0, a1, p.part32, O, 4 * stride, k0 * stride, wm, v0, v1,
+                      [&](int u) __attribute__((always_inline)) { return wk[u]; });
     k0 += 4 * U;
     if (k0 >= s) break;
     load_batch(k0);
@@ -1575,24 +1685,16 @@ static void launch_k(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, h
   else hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
 }
 
-template <bool REDO>
-static void launch_split_t(const SplitParams& p, int dtype, bool paged, dim3 grid, hipStream_t stream,
-                           hipEvent_t t0, hipEvent_t t1) {
-  const dim3 block(kThreads);
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream,
+                        hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(grid_x, grid_y), block(kThreads);
   if (dtype == MLA_DTYPE_F16) {
-    if (paged) launch_k(split_kernel<MLA_DTYPE_F16, true, REDO>, grid, block, stream, t0, t1, p);
-    else launch_k(split_kernel<MLA_DTYPE_F16, false, REDO>, grid, block, stream, t0, t1, p);
+    if (paged) launch_k(split_kernel<MLA_DTYPE_F16, true>, grid, block, stream, t0, t1, p);
+    else launch_k(split_kernel<MLA_DTYPE_F16, false>, grid, block, stream, t0, t1, p);
   } else {
-    if (paged) launch_k(split_kernel<MLA_DTYPE_BF16, true, REDO>, grid, block, stream, t0, t1, p);
-    else launch_k(split_kernel<MLA_DTYPE_BF16, false, REDO>, grid, block, stream, t0, t1, p);
+    if (paged) launch_k(split_kernel<MLA_DTYPE_BF16, true>, grid, block, stream, t0, t1, p);
+    else launch_k(split_kernel<MLA_DTYPE_BF16, false>, grid, block, stream, t0, t1, p);
   }
-}
-
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, bool redo,
-                        hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid(grid_x, grid_y);
-  if (redo) launch_split_t<true>(p, dtype, paged, grid, stream, t0, t1);
-  else launch_split_t<false>(p, dtype, paged, grid, stream, t0, t1);
   return hipGetLastError();
 }
 

@@ -156,10 +156,12 @@ int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32
 
 /*
  * Bytes of device workspace mla_decode needs for this description:
- *   plan (int32): B + (B+1) + 4*max_work, then max_work * ceil(H/128)
- *   rerun flags, rounded to 256 bytes; partial lse (fp32, base 2): max_work * H, rounded to 256;
- *   partial out: max_work * H * 512 values, rounded to 256 bytes; fp16 for fp16
- *   inputs (the output's precision), fp32 for bf16 inputs.
+ *   plan (int32): B + (B+1) + 4*max_work, rounded to 256 bytes;
+ *   partial lse (fp32, base 2): max_work * H, rounded to 256 bytes;
+ *   partial rows (fp16, normalised): max_work * H * 512, rounded to 256 bytes;
+ *   fp32 copies of partial rows: max_work * H * 512, rounded to 256 bytes
+ *   (a split writes the fp32 copy of a row only when one of its values lies
+ *   beyond +-1, so that storing it in fp16 would cost more than 2^-12).
  */
 int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
 
@@ -202,11 +204,9 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *              aligned; its contents on entry do not matter.
  * A sequence with L_b = 0 gets out = 0 and lse = -inf.
  * Launches: the split kernel (in planner mode each of its workgroups runs the
- * planner rule itself and workgroup 0 writes the plan into the workspace); a
- * second split launch that only reruns work items whose scores spread beyond
- * the range of P for the reference max taken from their first tile (all other
- * workgroups exit at once); the combine kernel (only touches sequences with
- * s_b > 1; a single split writes out/lse directly).
+ * planner rule itself and workgroup 0 writes the plan into the workspace),
+ * then the combine kernel when any sequence has s_b > 1 (a single split
+ * writes out/lse directly).
  * Calls that share a workspace must be ordered on one stream.
  */
 int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
@@ -220,15 +220,16 @@ const char* mla_last_error(void);
 /*
  * Kernel timing for measurement.  While enabled, every mla_decode call times
  * its launches on its stream from their dispatch packets (start and stop
- * events of the launch itself): split_ms the split kernel's main launch,
- * rerun_ms the exact-max rerun launch, combine_ms the combine (0 when no
- * combine runs).
+ * events of the launch itself): split_ms the split kernel, combine_ms the
+ * combine (0 when no combine runs).  Events on the dispatch packets slow
+ * the launches down by a few percent; use them to split a call's time
+ * between its kernels, not as the call's time.
  * mla_timing_read() synchronises on those events and returns the summed
  * milliseconds and the number of calls since the last read (then resets).
  * Up to 4096 calls are recorded between reads; later ones are not timed.
  */
 int mla_timing_enable(int enable);
-int mla_timing_read(float* split_ms, float* rerun_ms, float* combine_ms, int32_t* calls);
+int mla_timing_read(float* split_ms, float* combine_ms, int32_t* calls);
 
 #ifdef __cplusplus
 }

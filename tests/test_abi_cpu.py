@@ -167,10 +167,11 @@ def test_workspace_size_formula(L):
         n = ctypes.c_size_t()
         assert L.mla_workspace_size(ctypes.byref(d), ns, cus, ctypes.byref(n)) == 0
         r = lambda x: -(-x // 256) * 256  # noqa: E731
-        plan = 4 * B + 4 * (B + 1) + 16 * want_w + 4 * want_w * hg
+        plan = 4 * B + 4 * (B + 1) + 16 * want_w
         part_lse = r(plan)
-        part_o = r(part_lse + 4 * want_w * H)
-        assert n.value == r(part_o + 512 * (2 if d.dtype == 0 else 4) * want_w * H)   # fp16 partials for fp16
+        part16 = r(part_lse + 4 * want_w * H)
+        part32 = r(part16 + 512 * 2 * want_w * H)
+        assert n.value == r(part32 + 512 * 4 * want_w * H)   # fp16 rows, fp32 copies of the wide ones
 
 
 def _plan(lens, heads, ns, cus, sq=1):

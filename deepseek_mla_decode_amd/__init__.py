@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     D_LATENT,
     D_ROPE,
     MAX_SPLITS,
+    NOALLOC_SCRATCH_BYTES,
     MLA_DTYPE_BF16,
     MLA_DTYPE_F16,
     SPLIT_BLOCK_ROWS,
@@ -23,7 +24,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "mla_decode", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
+    "mla_decode", "mla_decode_noalloc", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
     "mla_num_cus", "mla_last_error", "mla_timing_enable", "mla_timing_read", "make_desc",
     "MlaDesc", "MlaError",
 ]
@@ -130,9 +131,19 @@ def _workspace(device, stream_id: int, nbytes: int):
     return ws
 
 
+def mla_decode_noalloc(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
+                       num_split: int = 0, out=None, lse=None, stream=None) -> Tuple["object", "object"]:
+    """``mla_decode`` through the C ABI's no-allocation entry point: the
+    library's static per-GPU scratch array replaces the workspace (at most
+    ``NOALLOC_SCRATCH_BYTES``; calls that overlap on one GPU race).  Pass
+    ``out`` and ``lse`` to keep the call free of allocations."""
+    return mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out,
+                      lse, stream=stream, _noalloc=True)
+
+
 def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
                num_split: int = 0, out=None, lse=None, workspace=None,
-               stream=None) -> Tuple["object", "object"]:
+               stream=None, _noalloc: bool = False) -> Tuple["object", "object"]:
     """MLA decode through the C ABI; returns ``(out [B,H,512], lse fp32 [B,H])``.
 
     Contiguous cache: ``kv_latent [B, S, 1, 512]``, ``k_pe [B, S, 1, 64]``,
@@ -175,16 +186,22 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     _check_batch_arrays(B, cache_seqlens, block_table)
     desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q)
     s = torch.cuda.current_stream(q_nope.device) if stream is None else stream
+    kv = _as4(kv_latent, D_LATENT, "kv_latent")
+    kp = _as4(k_pe, D_ROPE, "k_pe")
+    bt = None if block_table is None else block_table.data_ptr()
+    if _noalloc:
+        st = _lib.lib().mla_decode_noalloc(
+            q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(), bt, cache_seqlens.data_ptr(),
+            float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc), s.cuda_stream)
+        _lib.check(st)
+        return (out4, lse4) if four_d else (out, lse)
     if workspace is None:
         need = mla_workspace_size(desc, num_split, mla_num_cus(q_nope.device.index))
         workspace = _workspace(q_nope.device, s.cuda_stream, need)
     elif not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor")
-    kv = _as4(kv_latent, D_LATENT, "kv_latent")
-    kp = _as4(k_pe, D_ROPE, "k_pe")
     st = _lib.lib().mla_decode(
-        q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(),
-        None if block_table is None else block_table.data_ptr(), cache_seqlens.data_ptr(),
+        q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(), bt, cache_seqlens.data_ptr(),
         float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), s.cuda_stream)
     _lib.check(st)

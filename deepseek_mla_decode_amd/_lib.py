@@ -21,6 +21,7 @@ D_LATENT = 512
 D_ROPE = 64
 SPLIT_BLOCK_ROWS = 64
 MAX_SPLITS = 1024
+NOALLOC_SCRATCH_BYTES = 100 << 20
 
 
 class MlaDesc(ctypes.Structure):
@@ -64,6 +65,8 @@ SIGNATURES = {
     "mla_plan_device": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
                                   ctypes.POINTER(MlaDesc), _P, ctypes.c_size_t, _P]),
+    "mla_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
+                                          ctypes.POINTER(MlaDesc), _P]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "mla_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _PI32]),

@@ -252,10 +252,13 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
   return ok();
 }
 
-int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
-               const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
-               int32_t num_split, void* out, float* lse, const mla_desc* d, void* workspace,
-               size_t workspace_bytes, hipStream_t stream) {
+// mla_decode and mla_decode_noalloc.  noalloc: the workspace is this
+// device's static scratch array (workspace / workspace_bytes are ignored);
+// nothing here allocates (no events either).
+static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                       int32_t num_split, void* out, float* lse, const mla_desc* d, void* workspace,
+                       size_t workspace_bytes, bool noalloc, hipStream_t stream) {
   int st;
   if ((st = check_desc(d)) != MLA_OK) return st;
   if ((st = check_num_split(num_split)) != MLA_OK) return st;
@@ -301,6 +304,13 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   int32_t max_work;
   if ((st = max_work_of(d, num_split, num_cus, &max_work)) != MLA_OK) return st;
   const Layout L = layout(d, max_work);
+  if (noalloc) {
+    if ((e = mla::noalloc_scratch(&workspace, &workspace_bytes)) != hipSuccess)
+      return fail(MLA_ERR_HIP, "no-allocation scratch: %s", hipGetErrorString(e));
+    if (L.total > workspace_bytes)
+      return fail(MLA_ERR_WORKSPACE, "this problem needs %zu bytes of workspace, beyond the %zu bytes of the "
+                  "no-allocation scratch (MLA_NOALLOC_SCRATCH_BYTES)", L.total, workspace_bytes);
+  }
   if (!workspace || workspace_bytes < L.total)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? workspace_bytes : 0, L.total);
   if (!aligned(workspace, 256)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -354,8 +364,9 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
   sp.num_cus = num_cus;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;
   // Timing (when enabled): each launch is timed from its dispatch packet.
+  // Not in the no-allocation form (creating events may allocate).
   TimingSlot ts;
-  hipEvent_t* ev = timing_slot(&ts) ? ts.ev : nullptr;
+  hipEvent_t* ev = !noalloc && timing_slot(&ts) ? ts.ev : nullptr;
   if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), stream,
                              ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
@@ -383,6 +394,21 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
     }
   }
   return ok();
+}
+
+int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+               const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+               int32_t num_split, void* out, float* lse, const mla_desc* d, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out, lse,
+                     d, workspace, workspace_bytes, false, stream);
+}
+
+int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                       int32_t num_split, void* out, float* lse, const mla_desc* d, hipStream_t stream) {
+  return decode_impl(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out, lse,
+                     d, nullptr, 0, true, stream);
 }
 
 int mla_timing_enable(int enable) {

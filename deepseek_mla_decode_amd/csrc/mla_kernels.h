@@ -59,6 +59,9 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+// This device's no-allocation scratch array: its device address (taken once
+// per device with hipGetSymbolAddress) and size (MLA_NOALLOC_SCRATCH_BYTES).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 // t0 / t1: events that time the launch from its dispatch packet, or null.
 hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream,
                         hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);

@@ -51,6 +51,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 namespace mla {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -1670,6 +1672,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point (mla_decode_noalloc): a static
+// device array, one per GPU the library runs on, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host the
+// name is only a stand-in for the device symbol): its device address is taken
+// once per device, with that device current, and cached.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  return hipSuccess;
+}
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);

@@ -214,6 +214,28 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
                int32_t num_split, void* out, float* lse, const mla_desc* desc, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * MLA decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and launches as
+ * mla_decode; the workspace is a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Nothing in this call allocates.  A problem whose
+ * workspace (mla_workspace_size) exceeds that size returns MLA_ERR_WORKSPACE
+ * and enqueues nothing.  A partial row (one work item, one query row) takes
+ * 3076 bytes of it, so 100 MiB holds about 34,000 of them: 256 work items of
+ * 128 query rows, for example, which is what the planner gives B = 64..256
+ * sequences of 128 heads on 256 CUs.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or other host threads) race and give wrong results.
+ * Calls on one stream are ordered and safe; the array's contents carry no
+ * meaning from one call to the next.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)100 << 20)
+int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                       int32_t num_split, void* out, float* lse, const mla_desc* desc, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char* mla_last_error(void);
 

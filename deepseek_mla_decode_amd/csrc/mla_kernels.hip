@@ -1251,15 +1251,19 @@ void split_kernel(SplitParams p) {
   store16(p.part16 + ((int64_t)split_slot * p.heads + h0) * 512, 512, bigrows);
   if (bigrows == 0) return;
   // fp32 rows of the large ones, in two halves of 256 values = 64 chunks of
-  // 4; this lane holds chunk 8 (vb % 8) + 2 q + g.
+  // 4; this lane holds chunk 8 (vb % 8) + 2 q + g.  The products are formed
+  // again from the accumulator (an opaque copy of inv keeps the compiler from
+  // holding the fp16 path's products, 256 registers, until here).
+  float inv32 = inv;
+  asm volatile("" : "+v"(inv32));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int vb = 8 * half; vb < 8 * half + 8; ++vb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 w = {acc[vb][4 * q + 0] * inv, acc[vb][4 * q + 1] * inv, acc[vb][4 * q + 2] * inv,
-                         acc[vb][4 * q + 3] * inv};
+        const f32x4 w = {acc[vb][4 * q + 0] * inv32, acc[vb][4 * q + 1] * inv32, acc[vb][4 * q + 2] * inv32,
+                         acc[vb][4 * q + 3] * inv32};
         *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage_at(hl_t, 8 * (vb & 7) + 2 * q + g_t)) = w;
       }
     }
@@ -1306,12 +1310,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Eight values (element offset e) of a partial row: fp16 rows in one 16-byte
-// read, fp32 rows in two.
-__device__ __forceinline__ void load_part16x8(const uint16_t* part16, int64_t e, f32x4& v0, f32x4& v1) {
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-  const u32x4 w = *reinterpret_cast<const u32x4*>(part16 + e);
-  v0 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.x, w.y}), f32x4);
-  v1 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{w.z, w.w}), f32x4);
+// read (kept as read until they are added, half the registers of fp32),
+// fp32 rows in two.
+__device__ __forceinline__ u32x4 load_part16x8(const uint16_t* part16, int64_t e) {
+  return *reinterpret_cast<const u32x4*>(part16 + e);
 }
 __device__ __forceinline__ void load_part32x8(const float* part32, int64_t e, f32x4& v0, f32x4& v1) {
   const f32x4* src = reinterpret_cast<const f32x4*>(part32 + e);
@@ -1319,11 +1321,15 @@ __device__ __forceinline__ void load_part32x8(const float* part32, int64_t e, f3
   v1 = src[1];
 }
 
-// a += w v for an fp16 partial row, or nothing when `skip`: a wide split,
-// whose fp16 slot holds stale bits (possibly NaN), or a batch entry past the
-// last split, which re-read the last one (possibly wide).  The product is
-// selected away rather than weighted by 0, since 0 * NaN is NaN.
-__device__ __forceinline__ void add_fp16_part(f32x4& a0, f32x4& a1, float w, f32x4 v0, f32x4 v1, bool skip) {
+// a += w v for an fp16 partial row (8 values as read), or nothing when
+// `skip`: a wide split, whose fp16 slot holds stale bits (possibly NaN), or a
+// batch entry past the last split, which re-read the last one (possibly
+// wide).  The product is selected away rather than weighted by 0, since
+// 0 * NaN is NaN.
+__device__ __forceinline__ void add_fp16_part(f32x4& a0, f32x4& a1, float w, u32x4 raw, bool skip) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const f32x4 v0 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{raw.x, raw.y}), f32x4);
+  const f32x4 v1 = __builtin_convertvector(__builtin_bit_cast(h4, u32x2{raw.z, raw.w}), f32x4);
   const f32x4 t0 = w * v0, t1 = w * v1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1333,25 +1339,31 @@ __device__ __forceinline__ void add_fp16_part(f32x4& a0, f32x4& a1, float w, f32
 }
 
 // a += w(u) v_u for the wide splits u of a batch of U (bit u of `wide`):
-// their fp32 rows at O + first + u * step, all read before any is added;
-// the other slots of the batch re-read the first wide row (a cache hit) and
-// add it with weight 0.  v0 / v1 are the batch's row registers, free by now.
+// their fp32 rows at O + first + u * step, read four at a time, each four
+// before any is added; the other slots of a four re-read the batch's first
+// wide row (a cache hit) and add it with weight 0.
 template <int U, typename WeightOf>
 __device__ __forceinline__ void add_fp32_parts(f32x4& a0, f32x4& a1, const float* part32, int64_t O, int64_t step,
-                                               int64_t first, uint32_t wide, f32x4 (&v0)[U], f32x4 (&v1)[U],
-                                               WeightOf weight_of) {
+                                               int64_t first, uint32_t wide, WeightOf weight_of) {
   if (wide == 0) return;
   const int f = __builtin_ctz(wide);
+  constexpr int G = U < 4 ? U : 4;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int uu = ((wide >> u) & 1u) ? u : f;
-    load_part32x8(part32, O + first + (int64_t)uu * step, v0[u], v1[u]);
-  }
+  for (int u0 = 0; u0 < U; u0 += G) {
+    if (((wide >> u0) & ((1u << G) - 1u)) == 0) continue;
+    f32x4 w0[G], w1[G];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float w = ((wide >> u) & 1u) ? weight_of(u) : 0.f;
-    a0 += w * v0[u];
-    a1 += w * v1[u];
+    for (int g = 0; g < G; ++g) {
+      const int u = u0 + g;
+      const int uu = ((wide >> u) & 1u) ? u : f;
+      load_part32x8(part32, O + first + (int64_t)uu * step, w0[g], w1[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float w = ((wide >> (u0 + g)) & 1u) ? weight_of(u0 + g) : 0.f;
+      a0 += w * w0[g];
+      a1 += w * w1[g];
+    }
   }
 }
 
@@ -1416,9 +1428,9 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
   // are read in the same round trip: they do not depend on the weights.
   const float r0 = lane_lse(L, p.heads, s, lane);
   const float r1 = S ? -__builtin_inff() : lane_lse(L, p.heads, s, lane + 64);
-  f32x4 v0[U], v1[U];
+  u32x4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_part16x8(p.part16, O + (int64_t)u * stride, v0[u], v1[u]);
+  for (int u = 0; u < U; ++u) v[u] = load_part16x8(p.part16, O + (int64_t)u * stride);
   __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
   const uint64_t wide = __builtin_amdgcn_ballot_w64(lse_flag(r0));   // bit k: split k has an fp32 row
   const CombineWeights cw = combine_weights(lse_value(r0), lse_value(r1), L, p.heads, s, lane);
@@ -1426,9 +1438,9 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const float w = lane_f32(cw.w_own, u);   // split u's weight, held by lane u
-    add_fp16_part(a0, a1, w, v0[u], v1[u], (wide >> u) & 1ull);
+    add_fp16_part(a0, a1, w, v[u], (wide >> u) & 1ull);
   }
-  add_fp32_parts<U>(a0, a1, p.part32, O, stride, 0, (uint32_t)(wide & ((1ull << U) - 1ull)), v0, v1,
+  add_fp32_parts<U>(a0, a1, p.part32, O, stride, 0, (uint32_t)(wide & ((1ull << U) - 1ull)),
                     [&](int u) __attribute__((always_inline)) { return lane_f32(cw.w_own, u); });
   if constexpr (S == 0) {
     // s > U: further batches of U; indices past s re-read split s - 1 with weight 0.
@@ -1438,20 +1450,20 @@ __device__ __forceinline__ void combine_head(const CombineParams& p, int b, int 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = k0 + u < s ? k0 + u : s - 1;
-        load_part16x8(p.part16, O + (int64_t)k * stride, v0[u], v1[u]);
+        v[u] = load_part16x8(p.part16, O + (int64_t)k * stride);
         lk[u] = L[(int64_t)k * p.heads];
       }
-      float wk[U];
+      auto weight_of = [&](int u) __attribute__((always_inline)) {
+        return any && k0 + u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
+      };
       uint32_t wm = 0;   // lk[u] is the same in every lane
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        wk[u] = any && k0 + u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
         const bool wd = k0 + u < s && lse_flag(lk[u]);
         wm |= wd ? 1u << u : 0u;
-        add_fp16_part(a0, a1, wk[u], v0[u], v1[u], wd || k0 + u >= s);
+        add_fp16_part(a0, a1, weight_of(u), v[u], wd || k0 + u >= s);
       }
-      add_fp32_parts<U>(a0, a1, p.part32, O, stride, (int64_t)k0 * stride, wm, v0, v1,
-                        [&](int u) __attribute__((always_inline)) { return wk[u]; });
+      add_fp32_parts<U>(a0, a1, p.part32, O, stride, (int64_t)k0 * stride, wm, weight_of);
     }
   }
   u32x4 r;
@@ -1524,13 +1536,13 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   const float l0 = lse_value(lane_lse(L, p.heads, s, lane)), l1 = lse_value(lane_lse(L, p.heads, s, lane + 64));
   // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
   // s re-read split s - 1, which then gets weight 0.
-  f32x4 v0[U], v1[U];
+  u32x4 v[U];
   float lk[U];
   auto load_batch = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
-      load_part16x8(p.part16, O + (int64_t)k * stride, v0[u], v1[u]);
+      v[u] = load_part16x8(p.part16, O + (int64_t)k * stride);
       lk[u] = L[(int64_t)k * p.heads];
     }
   };
@@ -1542,18 +1554,18 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = wave;;) {
-    float wk[U];
+    auto weight_of = [&](int u) __attribute__((always_inline)) {
+      return any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
+    };
     uint32_t wm = 0;   // lk[u] is the same in every lane
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      wk[u] = any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
       const bool wd = k0 + 4 * u < s && lse_flag(lk[u]);
       wm |= wd ? 1u << u : 0u;
-      add_fp16_part(a0, a1, wk[u], v0[u], v1[u], wd || k0 + 4 * u >= s);
+      add_fp16_part(a0, a1, weight_of(u), v[u], wd || k0 + 4 * u >= s);
     }
     // Splits k0 + 4 u: the fp32 rows of the wide ones (stride 4 splits).
-    add_fp32_parts<U>(a0, a1, p.part32, O, 4 * stride, k0 * stride, wm, v0, v1,
-                      [&](int u) __attribute__((always_inline)) { return wk[u]; });
+    add_fp32_parts<U>(a0, a1, p.part32, O, 4 * stride, k0 * stride, wm, weight_of);
     k0 += 4 * U;
     if (k0 >= s) break;
     load_batch(k0);

@@ -58,7 +58,37 @@ def cast_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def storage_np_dtype(dtype: str):
-    return {"f16": np.float16, "bf16": np.uint16}[dtype]
+    return {"f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+
+
+# FP8 cache: OCP E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits; no infinities; 0x7F / 0xFF are NaN; largest finite 448), one fp32
+# scale per cache tensor: a stored byte stands for decode(byte) * kv_scale.
+E4M3_MAX = 448.0
+DEFAULT_KV_SCALE = 0.0125   # N(0,1) values up to about 5.6 land below 448 / scale
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Magnitudes of the finite non-negative E4M3 codes 0x00..0x7E, ascending."""
+    out = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        out[code] = np.ldexp(m, -9) if e == 0 else np.ldexp(8 + m, e - 10)
+    return out
+
+
+def f32_to_e4m3_bits(x: np.ndarray, kv_scale: float) -> np.ndarray:
+    """Quantise x / kv_scale to E4M3 bytes: round to nearest, ties to an even
+    code, magnitudes beyond 448 saturate to 448 (input generation only)."""
+    a = np.abs(np.asarray(x, dtype=np.float64) / kv_scale)
+    mags = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a), 1, 126)
+    lo = hi - 1
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= mags[126], 126, code).astype(np.uint8)
+    sign = (np.signbit(np.asarray(x, dtype=np.float64))).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
 
 
 def _normal_rows(seed_seq: np.random.SeedSequence, n_rows: int, width: int, dtype: str) -> np.ndarray:
@@ -97,7 +127,13 @@ class MlaInputs:
     block_table: Optional[np.ndarray] = None  # paged: int32 [B, max_blocks]
     page_block_size: int = 0
     seqlen_q: int = 1             # query tokens per sequence (rows of q are token-major)
+    kv_dtype: str = ""            # cache storage: "" = as the queries, or "fp8" (E4M3 bytes)
+    kv_scale: float = 1.0         # fp8 cache: value = decode(byte) * kv_scale
     meta: dict = field(default_factory=dict)
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def paged(self) -> bool:
@@ -127,38 +163,63 @@ def make_queries(ss: np.random.SeedSequence, batch: int, heads: int, dtype: str)
     return np.ascontiguousarray(q[:, :, :D_LATENT]), np.ascontiguousarray(q[:, :, D_LATENT:])
 
 
+def _cache_rows(seed_seq, n_rows: int, dtype: str, kv_dtype: str, kv_scale: float) -> np.ndarray:
+    """N(0,1) cache rows in the storage format: 16-bit as the queries, or E4M3
+    bytes of value / kv_scale."""
+    if kv_dtype != "fp8":
+        return _normal_rows(seed_seq, n_rows, D_QK, dtype)
+    return f32_to_e4m3_bits(_normal_rows(seed_seq, n_rows, D_QK, "f16").astype(np.float32), kv_scale)
+
+
+def _kv_args(kv_dtype, kv_scale):
+    kv_dtype = kv_dtype or ""
+    if kv_dtype not in ("", "fp8"):
+        raise ValueError(f"unknown cache dtype {kv_dtype!r}")
+    if kv_dtype == "fp8":
+        return kv_dtype, float(DEFAULT_KV_SCALE if kv_scale is None else kv_scale)
+    return kv_dtype, 1.0
+
+
 def make_contiguous(batch: int, heads: int, max_seqlen: int, cache_seqlens, dtype: str = "f16",
-                    seed: int = 0, scale: Optional[float] = None, seqlen_q: int = 1) -> MlaInputs:
+                    seed: int = 0, scale: Optional[float] = None, seqlen_q: int = 1,
+                    kv_dtype: Optional[str] = None, kv_scale: Optional[float] = None) -> MlaInputs:
     """Contiguous cache ``[B, S, 1, 512] + [B, S, 1, 64]``, all rows N(0,1).
 
     With ``seqlen_q`` > 1 each sequence has that many query tokens of ``heads``
-    heads each, stored as ``seqlen_q * heads`` query rows, token-major."""
+    heads each, stored as ``seqlen_q * heads`` query rows, token-major.
+    ``kv_dtype="fp8"`` stores the cache as E4M3 bytes of value / kv_scale
+    (the rows drawn as for fp16, then quantised)."""
+    kv_dtype, kv_scale = _kv_args(kv_dtype, kv_scale)
     lens = np.asarray(cache_seqlens, dtype=np.int32).reshape(batch)
     if lens.size and (lens.min() < 0 or lens.max() > max_seqlen):
         raise ValueError("cache_seqlens must lie in [0, max_seqlen]")
     root = np.random.SeedSequence(seed)
     sq, skv = root.spawn(2)
     q_nope, q_pe = make_queries(sq, batch, heads * seqlen_q, dtype)
-    rows = _normal_rows(skv, batch * max_seqlen, D_QK, dtype).reshape(batch, max_seqlen, 1, D_QK)
+    rows = _cache_rows(skv, batch * max_seqlen, dtype, kv_dtype, kv_scale).reshape(batch, max_seqlen, 1, D_QK)
     return MlaInputs(
         dtype=dtype, q_nope=q_nope, q_pe=q_pe, cache_seqlens=lens,
         softmax_scale=default_scale() if scale is None else float(scale),
         kv_latent=np.ascontiguousarray(rows[..., :D_LATENT]),
         k_pe=np.ascontiguousarray(rows[..., D_LATENT:]), seqlen_q=seqlen_q,
+        kv_dtype=kv_dtype, kv_scale=kv_scale,
         meta={"layout": "contiguous", "seed": seed, "max_seqlen": max_seqlen},
     )
 
 
 def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed: int = 0,
                page_block_size: int = 64, max_blocks: Optional[int] = None, shuffle: bool = True,
-               spare_pages: int = 0, scale: Optional[float] = None, seqlen_q: int = 1) -> MlaInputs:
+               spare_pages: int = 0, scale: Optional[float] = None, seqlen_q: int = 1,
+               kv_dtype: Optional[str] = None, kv_scale: Optional[float] = None) -> MlaInputs:
     """Paged pool ``[P, page, 1, 576]`` with a block_table.
 
     Each sequence owns ``ceil(L_b / page)`` logical pages.  Physical pages are a
     random permutation of ``0..P-1`` (``shuffle``) handed to logical pages in
     order; unused block_table entries are -1.  ``spare_pages`` adds pool pages
-    that no sequence references.
+    that no sequence references.  ``kv_dtype="fp8"``: E4M3 pool bytes (see
+    make_contiguous).
     """
+    kv_dtype, kv_scale = _kv_args(kv_dtype, kv_scale)
     lens = np.asarray(cache_seqlens, dtype=np.int32).reshape(batch)
     if lens.size and lens.min() < 0:
         raise ValueError("cache_seqlens must be >= 0")
@@ -173,7 +234,7 @@ def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed:
     root = np.random.SeedSequence(seed)
     sq, skv, sperm = root.spawn(3)
     q_nope, q_pe = make_queries(sq, batch, heads * seqlen_q, dtype)
-    pool = _normal_rows(skv, max(n_pages, 1) * page_block_size, D_QK, dtype)
+    pool = _cache_rows(skv, max(n_pages, 1) * page_block_size, dtype, kv_dtype, kv_scale)
     pool = pool.reshape(max(n_pages, 1), page_block_size, 1, D_QK)
     perm = np.random.default_rng(sperm).permutation(n_pages) if shuffle else np.arange(n_pages)
     table = np.full((batch, max_blocks), -1, dtype=np.int32)
@@ -186,6 +247,7 @@ def make_paged(batch: int, heads: int, cache_seqlens, dtype: str = "bf16", seed:
         dtype=dtype, q_nope=q_nope, q_pe=q_pe, cache_seqlens=lens,
         softmax_scale=default_scale() if scale is None else float(scale),
         pool=pool, block_table=table, page_block_size=page_block_size, seqlen_q=seqlen_q,
+        kv_dtype=kv_dtype, kv_scale=kv_scale,
         meta={"layout": "paged", "seed": seed, "n_pages": n_pages},
     )
 
@@ -197,6 +259,8 @@ def scale_random_rows(inp: MlaInputs, fraction: float, factor: float, seed: int)
     With a power-of-two factor the result is exact in fp16/bf16 storage.
     Returns the chosen logical positions as an int array ``[B, k_max]`` (-1 padded).
     """
+    if inp.cache_dtype == "fp8":
+        raise ValueError("scale_random_rows works on 16-bit caches (an E4M3 row times 8 may saturate)")
     rng = np.random.default_rng(seed)
     chosen = []
     for b in range(inp.batch):

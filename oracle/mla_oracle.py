@@ -66,13 +66,33 @@ SPLIT_BLOCK_ROWS = 64
 # ---------------------------------------------------------------------------
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 value of fp16 (numpy float16) or bf16 (uint16 bits) storage."""
+    """Exact float64 value of fp16 (numpy float16), bf16 (uint16 bits) or
+    fp8 (uint8 bytes, OCP E4M3) storage."""
     if dtype == "f16":
         return np.asarray(a, dtype=np.float16).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_to_f64(a)
     raise ValueError(dtype)
+
+
+def e4m3_to_f64(a: np.ndarray) -> np.ndarray:
+    """OCP 8-bit E4M3 bytes to exact float64: sign bit 7, exponent bits 6..3
+    (bias 7), mantissa bits 2..0.  Exponent 0 is subnormal, (m / 8) * 2^-6;
+    otherwise (1 + m / 8) * 2^(e - 7).  Exponent 15 with mantissa 7 is NaN
+    (0x7F, 0xFF); the format has no infinities, so the largest finite
+    magnitude is 1.75 * 2^8 = 448.  The FP8 cache the TileLang guide lists
+    among its variant kernels ("变体内核") gives no format; this is the
+    reading this library takes (one fp32 scale per cache tensor)."""
+    b = np.asarray(a, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (b & 0x7 == 7), np.nan, mag)
+    return sign * mag
 
 
 # ---------------------------------------------------------------------------
@@ -80,19 +100,23 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def cache_rows(b: int, L: int, dtype: str, *, kv_latent=None, k_pe=None, pool=None,
-               block_table=None, page_block_size: int = 0) -> np.ndarray:
-    """Rows 0..L-1 of sequence b as float64 ``[L, 576]`` (latent then RoPE)."""
+               block_table=None, page_block_size: int = 0, kv_scale: float = 1.0) -> np.ndarray:
+    """Rows 0..L-1 of sequence b as float64 ``[L, 576]`` (latent then RoPE).
+    ``dtype`` is the cache's storage; an fp8 cache's values are the decoded
+    bytes times ``kv_scale``."""
     if L == 0:
         return np.zeros((0, D_LATENT + D_ROPE))
     if pool is None:
         lat = to_f64(kv_latent[b, :L, 0, :], dtype)
         pe = to_f64(k_pe[b, :L, 0, :], dtype)
-        return np.concatenate([lat, pe], axis=1)
-    j = np.arange(L)
-    pages = np.asarray(block_table)[b, j // page_block_size]
-    if pages.min() < 0 or pages.max() >= pool.shape[0]:
-        raise IndexError("block_table references a page outside the pool")
-    return to_f64(pool[pages, j % page_block_size, 0, :], dtype)
+        rows = np.concatenate([lat, pe], axis=1)
+    else:
+        j = np.arange(L)
+        pages = np.asarray(block_table)[b, j // page_block_size]
+        if pages.min() < 0 or pages.max() >= pool.shape[0]:
+            raise IndexError("block_table references a page outside the pool")
+        rows = to_f64(pool[pages, j % page_block_size, 0, :], dtype)
+    return rows * kv_scale if dtype == "fp8" else rows
 
 
 # ---------------------------------------------------------------------------
@@ -132,9 +156,16 @@ def attend(qn: np.ndarray, qp: np.ndarray, K: np.ndarray, softmax_scale: float):
 # ---------------------------------------------------------------------------
 
 def _layout_kwargs(inp) -> dict:
+    kw = dict(kv_scale=float(getattr(inp, "kv_scale", 1.0)))
     if inp.pool is not None:
-        return dict(pool=inp.pool, block_table=inp.block_table, page_block_size=inp.page_block_size)
-    return dict(kv_latent=inp.kv_latent, k_pe=inp.k_pe)
+        kw.update(pool=inp.pool, block_table=inp.block_table, page_block_size=inp.page_block_size)
+    else:
+        kw.update(kv_latent=inp.kv_latent, k_pe=inp.k_pe)
+    return kw
+
+
+def _cache_dtype(inp) -> str:
+    return getattr(inp, "kv_dtype", "") or inp.dtype
 
 
 def visible_rows(L: int, seqlen_q: int, t: int) -> int:
@@ -161,7 +192,7 @@ def mla_decode_ref(inp, batches: Optional[Sequence[int]] = None,
     kw = _layout_kwargs(inp)
     for i, b in enumerate(bsel):
         L = max(int(inp.cache_seqlens[b]), 0)
-        K = cache_rows(b, L, inp.dtype, **kw)
+        K = cache_rows(b, L, _cache_dtype(inp), **kw)
         for t in range(sq):
             idx = np.nonzero(hsel // hpt == t)[0]
             if idx.size == 0:
@@ -240,7 +271,7 @@ def mla_decode_split_ref(inp, splits, batches: Optional[Sequence[int]] = None,
     for i, b in enumerate(bsel):
         s = splits if np.isscalar(splits) else splits[b]
         L = max(int(inp.cache_seqlens[b]), 0)
-        K = cache_rows(b, L, inp.dtype, **kw)
+        K = cache_rows(b, L, _cache_dtype(inp), **kw)
         for t in range(sq):
             idx = np.nonzero(hsel // hpt == t)[0]
             if idx.size == 0:

@@ -324,7 +324,79 @@ def pin_golden(orc):
         _close(lse[0], case["lse"], 1e-14, 1e-15, f"golden {case['name']} lse")
 
 
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) cache with a per-tensor scale
+# ---------------------------------------------------------------------------
+
+# Bytes decoded by hand from the format (sign | 4 exponent bits, bias 7 | 3
+# mantissa bits; exponent 0 subnormal with 2^-6 * m/8; no infinities).
+E4M3_TABLE = [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x02, 2.0 ** -8), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+    (0x0F, 1.875 * 2.0 ** -6), (0x30, 0.5), (0x38, 1.0), (0x39, 1.125), (0x3C, 1.5), (0x40, 2.0),
+    (0x48, 4.0), (0x70, 128.0), (0x77, 240.0), (0x78, 256.0), (0x7E, 448.0), (0x80, -0.0),
+    (0xB8, -1.0), (0xBC, -1.5), (0xFE, -448.0), (0x81, -(2.0 ** -9)),
+]
+
+
+def pin_fp8_decode(orc):
+    """Hand-decoded E4M3 bytes; 0x7F and 0xFF are NaN."""
+    codes = np.array([c for c, _ in E4M3_TABLE], dtype=np.uint8)
+    vals = orc.to_f64(codes, "fp8")
+    for (c, v), got in zip(E4M3_TABLE, vals):
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), f"E4M3 0x{c:02X}: {got} != {v}"
+    assert np.isnan(orc.to_f64(np.array([0x7F, 0xFF], dtype=np.uint8), "fp8")).all()
+
+
+def _fp8_twin(inp8, dtype):
+    """The 16-bit problem whose cache holds exactly the fp8 cache's values
+    (kv_scale a power of two, so every value is an fp16 / bf16 number): the
+    values come from the generator's E4M3 table, not from the oracle."""
+    import copy
+    mags = mi._e4m3_magnitudes()
+    def val(b):
+        b = np.asarray(b, dtype=np.int64)
+        v = mags[np.minimum(b & 0x7F, 126)] * np.where(b & 0x80, -1.0, 1.0)
+        return mi.cast_storage((v * inp8.kv_scale).astype(np.float32), dtype)
+    twin = copy.copy(inp8)
+    twin.kv_dtype, twin.kv_scale = "", 1.0
+    if inp8.paged:
+        twin.pool = val(inp8.pool)
+    else:
+        twin.kv_latent, twin.k_pe = val(inp8.kv_latent), val(inp8.k_pe)
+    return twin
+
+
+def pin_fp8_matches_16bit(orc):
+    """An fp8 cache with kv_scale = 2^-3 gives exactly the result of the
+    16-bit cache holding the same values, contiguous and paged."""
+    for inp8 in (mi.make_contiguous(2, 3, 70, [70, 33], "f16", seed=31, kv_dtype="fp8", kv_scale=0.125),
+                 mi.make_paged(2, 2, [40, 65], "bf16", seed=32, page_block_size=32, kv_dtype="fp8",
+                               kv_scale=0.125)):
+        twin = _fp8_twin(inp8, inp8.dtype)
+        o8, l8 = orc.mla_decode_ref(inp8)
+        o16, l16 = orc.mla_decode_ref(twin)
+        assert np.array_equal(o8, o16) and np.array_equal(l8, l16), "fp8 cache differs from its 16-bit twin"
+
+
+def pin_fp8_scale(orc):
+    """kv_scale s multiplies every cache value: the same as scores scaled by s
+    (softmax_scale * s) and the output times s, for a scale that is not a
+    power of two."""
+    inp = mi.make_contiguous(2, 3, 50, [50, 7], "f16", seed=33, kv_dtype="fp8", kv_scale=0.0123)
+    o, l = orc.mla_decode_ref(inp)
+    import copy
+    unit = copy.copy(inp)
+    unit.kv_scale = 1.0
+    unit.softmax_scale = inp.softmax_scale * 0.0123
+    ou, lu = orc.mla_decode_ref(unit)
+    _close(o, 0.0123 * ou, 1e-12, 1e-15, "fp8 scale out")
+    _close(l, lu, 1e-12, 1e-12, "fp8 scale lse")
+
+
 ALL_PINS = [
+    pin_fp8_decode,
+    pin_fp8_matches_16bit,
+    pin_fp8_scale,
     pin_golden,
     pin_seqlen1,
     pin_uniform,

@@ -60,3 +60,19 @@ def test_config_shapes_small():
     c3 = mi.make_config(3, batch_subset=2)
     assert c3.block_table.shape == (2, 256) and c3.dtype == "bf16"
     assert 1 <= c3.cache_seqlens.min() and c3.cache_seqlens.max() <= 16384
+
+
+def test_e4m3_encoder_round_trip_ties_and_saturation():
+    """The generator's E4M3 quantiser: every finite magnitude times the scale
+    encodes to its own code; a value halfway between two codes goes to the
+    even code; magnitudes beyond 448 saturate; the sign is bit 7."""
+    s = 0.5
+    mags = mi._e4m3_magnitudes()
+    codes = mi.f32_to_e4m3_bits(mags * s, s)
+    assert np.array_equal(codes, np.arange(127, dtype=np.uint8))
+    assert np.array_equal(mi.f32_to_e4m3_bits(-mags[1:] * s, s), (np.arange(1, 127) | 0x80).astype(np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2 * s
+    got = mi.f32_to_e4m3_bits(mids, s).astype(np.int64)
+    lo = np.arange(126)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert (mi.f32_to_e4m3_bits(np.array([449.0, 1e6, -1e6]) * s, s) == np.array([0x7E, 0x7E, 0xFE])).all()

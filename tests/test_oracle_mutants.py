@@ -37,6 +37,10 @@ MUTANTS = {
     "causal_direction": ("max(int(L), 0) - (seqlen_q - 1 - t)", "max(int(L), 0) - t"),
     "causal_offset": ("max(int(L), 0) - (seqlen_q - 1 - t)", "max(int(L), 0) - (seqlen_q - t)"),
     "token_major_rows": ("hsel // hpt == t", "hsel % sq == t"),
+    "fp8_bias": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
+    "fp8_subnormal": ("m / 8.0 * 2.0 ** -6", "m / 8.0 * 2.0 ** -7"),
+    "fp8_mantissa": ("(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),
+    "fp8_no_scale": ('return rows * kv_scale if dtype == "fp8" else rows', "return rows"),
 }
 
 

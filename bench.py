@@ -39,19 +39,19 @@ D_QK, D_V = 576, 512
 METRIC = "MLA decode TFLOPS + KV GB/s (% roofline), B=64/128 h=128 d=576/512"
 
 
-def workload_figures(lens, heads: int, seqlen_q: int = 1):
+def workload_figures(lens, heads: int, seqlen_q: int = 1, kv_elt: int = 2):
     """Algorithmic flops and bytes of one call (cache rows, Q, out, lse).
 
     `heads` counts query rows (seqlen_q tokens x heads per token); with several
     query tokens, token t of s is charged only the L - (s - 1 - t) rows it
-    sees."""
+    sees.  kv_elt: bytes per cache value (2, or 1 for an FP8 cache)."""
     import numpy as np
     L = np.maximum(np.asarray(lens, dtype=np.int64), 0)
     rows = float(np.sum(L))
     B, s = len(lens), seqlen_q
     seen = float(sum(np.sum(np.maximum(L - (s - 1 - t), 0)) for t in range(s)))
     flops = 2.0 * (heads // s) * (D_QK + D_V) * seen
-    kv_bytes = rows * D_QK * 2
+    kv_bytes = rows * D_QK * kv_elt
     total_bytes = kv_bytes + B * heads * (D_QK * 2 + D_V * 2 + 4)
     return flops, kv_bytes, total_bytes
 
@@ -129,7 +129,7 @@ def cpu_baseline(inp, budget_s: float):
         oracle.mla_decode_ref(inp, batches=[done])
         done += 1
     el = time.perf_counter() - t0
-    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads, inp.seqlen_q)
+    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads, inp.seqlen_q)   # flops only
     return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} query rows), fp64 NumPy, "
                       f"{el:.1f} s wall",
@@ -152,6 +152,8 @@ def main() -> int:
                     help="query heads per token instead of the workload's (e.g. one tensor-parallel shard)")
     ap.add_argument("--seqlen-q", type=int, default=1,
                     help="query tokens per sequence (speculative / multi-token decode), each of H heads")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="store the workload's cache as FP8 E4M3 bytes with one scale (workloads 0..3)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -167,10 +169,12 @@ def main() -> int:
     from mla_inputs.torch_io import to_device
 
     t_gen = time.perf_counter()
-    inp = mi.make_config(args.config, seqlen_q=args.seqlen_q, heads=args.heads or None)
+    inp = mi.make_config(args.config, seqlen_q=args.seqlen_q, heads=args.heads or None,
+                         kv_dtype="fp8" if args.kv_fp8 else None)
     gen_s = time.perf_counter() - t_gen
     dev = to_device(inp, "cuda")
-    flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads, inp.seqlen_q)
+    kv_elt = 1 if inp.cache_dtype == "fp8" else 2
+    flops, kv_bytes, total_bytes = workload_figures(inp.cache_seqlens, inp.heads, inp.seqlen_q, kv_elt)
     # Rotate copies of the cache when one copy would fit in the 256 MiB last-level cache.
     copies = args.copies or (1 if kv_bytes > 1.5 * 2**30 else 3)
     devs = [dev]
@@ -187,7 +191,7 @@ def main() -> int:
     outs = [torch.empty((B, H, 512), dtype=dev["q_nope"].dtype, device="cuda") for _ in devs]
     lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in devs]
     desc = mla.make_desc(dev["q_nope"], dev["q_pe"], dev["kv_latent"], dev["k_pe"], dev["block_table"], outs[0],
-                         seqlen_q=S)
+                         seqlen_q=S, kv_scale=dev["kv_scale"])
     ws = torch.empty(mla.mla_workspace_size(desc, args.num_split, mla.mla_num_cus()), dtype=torch.uint8,
                      device="cuda")
 
@@ -198,7 +202,8 @@ def main() -> int:
         d = devs[i % len(devs)]
         mla.mla_decode(tokens(d["q_nope"]), tokens(d["q_pe"]), d["kv_latent"], d["k_pe"],
                        d["block_table"], d["cache_seqlens"], inp.softmax_scale, num_split=args.num_split,
-                       out=tokens(outs[i % len(devs)]), lse=tokens(lses[i % len(devs)]), workspace=ws)
+                       out=tokens(outs[i % len(devs)]), lse=tokens(lses[i % len(devs)]), workspace=ws,
+                       kv_scale=d["kv_scale"])
 
     for i in range(args.warmup):
         step(i)
@@ -242,7 +247,7 @@ def main() -> int:
 
     cpu = cpu_baseline(inp, args.cpu_budget) if args.cpu_budget > 0 else None
 
-    workload = (mi.CONFIG_NAMES[args.config] + (f"_q{S}" if S > 1 else "")
+    workload = (inp.meta["config"] + (f"_q{S}" if S > 1 else "")
                 + (f"_heads{H // S}" if args.heads else ""))
     tflops = flops / (ms * 1e-3) / 1e12
     ai = flops / total_bytes
@@ -264,6 +269,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1), no dataset)",
         "config": {"workload": workload, "batch": B, "heads": H // S, "seqlen_q": S,
                    "seqlen_kv_mean": mean_L, "layout": "paged" if inp.paged else "contiguous",
+                   "kv_cache": "fp8_e4m3 (one scale)" if kv_elt == 1 else inp.dtype,
                    "num_split": args.num_split or "planner", "input_copies": len(devs)},
         "us_per_call": round(ms * 1e3, 2),
         "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES,
     MLA_DTYPE_BF16,
     MLA_DTYPE_F16,
+    MLA_KV_AS_DTYPE,
+    MLA_KV_FP8_E4M3,
     SPLIT_BLOCK_ROWS,
     MlaDesc,
     MlaError,
@@ -44,6 +46,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float16 or bfloat16")
 
 
+def _is_fp8_cache(t) -> bool:
+    """E4M3 cache bytes: a uint8 tensor, or PyTorch's float8_e4m3fn (the same
+    OCP E4M3 format)."""
+    torch = _torch()
+    return t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None)
+
+
 def _as4(t, last: int, name: str):
     """View a cache tensor as [N, rows, 1, last] (accepts [N, rows, last] too)."""
     if t.dim() == 3:
@@ -67,10 +76,13 @@ def mla_num_cus(device: Optional[int] = None) -> int:
     return n.value
 
 
-def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q: int = 1) -> MlaDesc:
+def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q: int = 1,
+              kv_scale: Optional[float] = None) -> MlaDesc:
     """Fill an ``MlaDesc`` from tensors (strides in elements).  With
     ``seqlen_q`` > 1 the H query rows are seqlen_q tokens x H / seqlen_q heads,
-    token-major."""
+    token-major.  An FP8 cache (``uint8`` or ``float8_e4m3fn`` E4M3 bytes)
+    stands for decode(byte) * ``kv_scale`` (default 1); a 16-bit cache takes
+    no scale."""
     if q_nope.dim() != 3 or q_nope.shape[2] != D_LATENT or q_nope.stride(2) != 1:
         raise ValueError(f"q_nope must be [B, H, 512] with contiguous last dim, got {tuple(q_nope.shape)}")
     B, H = q_nope.shape[0], q_nope.shape[1]
@@ -87,9 +99,18 @@ def make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q: int = 1
     d.seqlen_q = int(seqlen_q)
     d.d_latent, d.d_rope = D_LATENT, D_ROPE
     d.dtype = _dtype_code(q_nope)
-    for t, nm in ((q_pe, "q_pe"), (kv, "kv_latent"), (kp, "k_pe"), (out, "out")):
+    fp8 = _is_fp8_cache(kv)
+    if fp8 != _is_fp8_cache(kp):
+        raise TypeError(f"kv_latent ({kv.dtype}) and k_pe ({kp.dtype}) must share one storage type")
+    cache = () if fp8 else ((kv, "kv_latent"), (kp, "k_pe"))
+    for t, nm in ((q_pe, "q_pe"), (out, "out"), *cache):
         if t.dtype != q_nope.dtype:
             raise TypeError(f"{nm} dtype {t.dtype} differs from q_nope dtype {q_nope.dtype}")
+    if fp8:
+        d.kv_dtype = MLA_KV_FP8_E4M3
+        d.kv_scale = 1.0 if kv_scale is None else float(kv_scale)
+    elif kv_scale is not None and float(kv_scale) != 1.0:
+        raise ValueError("kv_scale applies to an FP8 cache only")
     if block_table is None:
         if kv.shape[0] != B:
             raise ValueError("contiguous cache must have batch as its first dimension")
@@ -132,18 +153,19 @@ def _workspace(device, stream_id: int, nbytes: int):
 
 
 def mla_decode_noalloc(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
-                       num_split: int = 0, out=None, lse=None, stream=None) -> Tuple["object", "object"]:
+                       num_split: int = 0, out=None, lse=None, stream=None,
+                       kv_scale: Optional[float] = None) -> Tuple["object", "object"]:
     """``mla_decode`` through the C ABI's no-allocation entry point: the
     library's static per-GPU scratch array replaces the workspace (at most
     ``NOALLOC_SCRATCH_BYTES``; calls that overlap on one GPU race).  Pass
     ``out`` and ``lse`` to keep the call free of allocations."""
     return mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out,
-                      lse, stream=stream, _noalloc=True)
+                      lse, stream=stream, kv_scale=kv_scale, _noalloc=True)
 
 
 def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
                num_split: int = 0, out=None, lse=None, workspace=None,
-               stream=None, _noalloc: bool = False) -> Tuple["object", "object"]:
+               stream=None, kv_scale: Optional[float] = None, _noalloc: bool = False) -> Tuple["object", "object"]:
     """MLA decode through the C ABI; returns ``(out [B,H,512], lse fp32 [B,H])``.
 
     Contiguous cache: ``kv_latent [B, S, 1, 512]``, ``k_pe [B, S, 1, 64]``,
@@ -152,6 +174,10 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     and ``block_table`` is int32 ``[B, max_blocks]``.  ``num_split=0`` lets the
     planner choose the splits.  Work is enqueued on ``stream`` (default: the
     current stream) and nothing synchronises.
+
+    FP8 cache: ``kv_latent`` / ``k_pe`` hold OCP E4M3 bytes (``uint8`` or
+    ``float8_e4m3fn``), standing for decode(byte) * ``kv_scale``; queries and
+    output stay float16 / bfloat16.
 
     Several query tokens per sequence: ``q_nope [B, s, H, 512]`` and ``q_pe
     [B, s, H, 64]`` (the s new tokens are the last s cache rows; token t sees
@@ -184,7 +210,7 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H):
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
     _check_batch_arrays(B, cache_seqlens, block_table)
-    desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q)
+    desc = make_desc(q_nope, q_pe, kv_latent, k_pe, block_table, out, seqlen_q, kv_scale)
     s = torch.cuda.current_stream(q_nope.device) if stream is None else stream
     kv = _as4(kv_latent, D_LATENT, "kv_latent")
     kp = _as4(k_pe, D_ROPE, "k_pe")

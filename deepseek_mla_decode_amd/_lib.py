@@ -17,6 +17,8 @@ STATUS_NAMES = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED
 
 MLA_DTYPE_F16 = 0
 MLA_DTYPE_BF16 = 1
+MLA_KV_AS_DTYPE = 0
+MLA_KV_FP8_E4M3 = 1
 D_LATENT = 512
 D_ROPE = 64
 SPLIT_BLOCK_ROWS = 64
@@ -41,6 +43,8 @@ class MlaDesc(ctypes.Structure):
         ("kv_sb", ctypes.c_int64), ("kv_sr", ctypes.c_int64),
         ("kpe_sb", ctypes.c_int64), ("kpe_sr", ctypes.c_int64),
         ("out_sb", ctypes.c_int64), ("out_sh", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("kv_scale", ctypes.c_float),
     ]
 
 

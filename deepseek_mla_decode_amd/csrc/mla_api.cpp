@@ -67,6 +67,15 @@ int check_desc(const mla_desc* d) {
                 d->d_rope);
   if (d->dtype != MLA_DTYPE_F16 && d->dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->kv_dtype != MLA_KV_AS_DTYPE && d->kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d not supported", d->kv_dtype);
+  if (d->kv_dtype == MLA_KV_FP8_E4M3) {
+    if (!std::isfinite(d->kv_scale) || !(d->kv_scale > 0.f))
+      return fail(MLA_ERR_INVALID_ARG, "kv_scale of an FP8 cache must be finite and positive");
+  } else if (d->kv_scale != 0.f && d->kv_scale != 1.f) {
+    return fail(MLA_ERR_INVALID_ARG, "kv_scale %g given for a 16-bit cache (only an FP8 cache is scaled)",
+                (double)d->kv_scale);
+  }
   if (d->seqlen_q < 0) return fail(MLA_ERR_INVALID_ARG, "seqlen_q %d < 0", d->seqlen_q);
   if (d->seqlen_q > mla::kMaxSeqlenQ)
     return fail(MLA_ERR_UNSUPPORTED, "seqlen_q %d above %d", d->seqlen_q, mla::kMaxSeqlenQ);
@@ -267,11 +276,18 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   if (d->batch == 0) return ok();
   if (!q_nope || !q_pe || !kv_latent || !k_pe || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "NULL data pointer");
+  // Element strides that keep rows 16-byte aligned: 8 16-bit elements, 16
+  // bytes of an FP8 cache.
+  const bool kv8 = d->kv_dtype == MLA_KV_FP8_E4M3;
   const int64_t strides[] = {d->q_nope_sb, d->q_nope_sh, d->q_pe_sb, d->q_pe_sh, d->kv_sb,
                              d->kv_sr,     d->kpe_sb,    d->kpe_sr,  d->out_sb,  d->out_sh};
-  for (int64_t s : strides) {
+  for (int i = 0; i < 10; ++i) {
+    const int64_t s = strides[i];
+    const int64_t unit = kv8 && i >= 4 && i < 8 ? 16 : 8;
     if (s < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride %lld", (long long)s);
-    if (s % 8) return fail(MLA_ERR_UNSUPPORTED, "stride %lld is not a multiple of 8 elements", (long long)s);
+    if (s % unit)
+      return fail(MLA_ERR_UNSUPPORTED, "stride %lld is not a multiple of %lld elements", (long long)s,
+                  (long long)unit);
   }
   if (d->kv_sr >= MLA_MAX_ROW_STRIDE || d->kpe_sr >= MLA_MAX_ROW_STRIDE || d->q_nope_sh >= MLA_MAX_ROW_STRIDE ||
       d->q_pe_sh >= MLA_MAX_ROW_STRIDE)
@@ -327,8 +343,8 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   mla::SplitParams sp{};
   sp.q_nope = static_cast<const uint16_t*>(q_nope);
   sp.q_pe = static_cast<const uint16_t*>(q_pe);
-  sp.kv = static_cast<const uint16_t*>(kv_latent);
-  sp.kpe = static_cast<const uint16_t*>(k_pe);
+  sp.kv = kv_latent;
+  sp.kpe = k_pe;
   sp.block_table = block_table;
   sp.seqlens = cache_seqlens;
   sp.num_splits = num_splits;
@@ -362,12 +378,16 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   sp.num_pages = paged ? d->num_pages : 0;
   sp.row_cap = row_cap;
   sp.num_cus = num_cus;
-  sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  // An FP8 cache's scale multiplies every score (folded into c) and the
+  // output (out_scale); the products use the stored values.
+  sp.scale_log2 = kv8 ? (float)((double)softmax_scale * (double)d->kv_scale * 1.4426950408889634)
+                      : softmax_scale * 1.4426950408889634f;
+  sp.out_scale = kv8 ? d->kv_scale : 1.f;
   // Timing (when enabled): each launch is timed from its dispatch packet.
   // Not in the no-allocation form (creating events may allocate).
   TimingSlot ts;
   hipEvent_t* ev = !noalloc && timing_slot(&ts) ? ts.ev : nullptr;
-  if ((e = mla::launch_split(sp, d->dtype, paged, max_work, mla::head_groups(d->heads), stream,
+  if ((e = mla::launch_split(sp, d->dtype, paged, kv8, max_work, mla::head_groups(d->heads), stream,
                              ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)) != hipSuccess)
     return fail(MLA_ERR_HIP, "split launch: %s", hipGetErrorString(e));
 

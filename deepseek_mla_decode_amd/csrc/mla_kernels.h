@@ -11,8 +11,8 @@ namespace mla {
 struct SplitParams {
   const uint16_t* q_nope;
   const uint16_t* q_pe;
-  const uint16_t* kv;           // latent part of cache rows
-  const uint16_t* kpe;          // RoPE part of cache rows
+  const void* kv;               // latent part of cache rows (16-bit, or E4M3 bytes)
+  const void* kpe;              // RoPE part of cache rows
   const int32_t* block_table;   // paged only
   const int32_t* seqlens;
   int32_t* num_splits;          // planner mode: written by workgroup 0 for the combine
@@ -34,7 +34,8 @@ struct SplitParams {
   int32_t num_pages;            // paged: page indices are clamped to [0, num_pages)
   int32_t row_cap;              // lengths are clamped to [0, row_cap]
   int32_t num_cus;              // planner mode: the planner's CU count
-  float scale_log2;             // softmax_scale * log2(e)
+  float scale_log2;             // softmax_scale * log2(e) (* kv_scale for an FP8 cache)
+  float out_scale;              // FP8 cache: kv_scale (values are decode(byte) * kv_scale); else 1
 };
 
 struct CombineParams {
@@ -63,8 +64,9 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 // per device with hipGetSymbolAddress) and size (MLA_NOALLOC_SCRATCH_BYTES).
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 // t0 / t1: events that time the launch from its dispatch packet, or null.
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream,
-                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// kv8: the cache holds E4M3 bytes (queries and output in `dtype`).
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, bool kv8, int grid_x, int grid_y,
+                        hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // mean_splits: splits per sequence, on average (forced count, or the plan's
 // bound over the batch); from kCombineSplitkMin on, four waves share a head.
 constexpr int kCombineSplitkMin = 16;

@@ -205,6 +205,19 @@ static_assert(kStages * kTileBytes + kQLdsBytes <= 160 * 1024, "LDS budget of a 
 __device__ __forceinline__ int swz_lat(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int n) { return (n >> 1) & 7; }
 
+// FP8 (E4M3) cache.  A tile arrives as bytes, [32][512] latent then [32][64]
+// RoPE, in one of two staging slots, and each wave widens the rows it loaded
+// itself into a 16-bit ring slot of the layout above (values as stored,
+// exactly: every E4M3 value is an fp16 and a bf16 value), so that the
+// products read the same operands as with a 16-bit cache.  The ring shrinks
+// to three slots; the two staging slots take the fourth one's place.
+constexpr int kLat8Bytes = kTileRows * 512;           // 16384
+constexpr int kTile8Bytes = kLat8Bytes + kTileRows * 64;   // 18432
+constexpr int kStages8 = 3;                           // 16-bit ring slots with an FP8 cache
+constexpr int kStaging8 = kStages8 * kTileBytes;      // first staging slot
+constexpr int kLoadsPerTile8 = 6;                     // DMA instructions per wave per FP8 tile
+static_assert(kStaging8 + 2 * kTile8Bytes == kStages * kTileBytes, "FP8 staging fills the fourth ring slot");
+
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
@@ -497,6 +510,53 @@ __device__ __forceinline__ void dma16_rope(const void* base, int w8, int nlast, 
       : "memory");
 }
 
+// FP8 tile loads.  Latent: one instruction moves two 512-byte rows, lane l
+// carrying bytes 16 (l % 32) .. + 15 of row n0 + l / 32 into lds_addr + 16 l;
+// base is row n0 (already clamped) and hi_off the byte offset of the second
+// row from it (0 when that row is past the last valid one, which is then
+// re-read).  RoPE: one 4-byte instruction moves four 64-byte rows, lane l
+// carrying bytes 4 (l % 16) .. + 3 of row n0 + l / 16 (clamped to nlast) into
+// lds_addr + 4 l.  Per-lane offsets are formed inside the asm, as in dma16.
+__device__ __forceinline__ void dma8_lat(const void* base, uint32_t hi_off, uint32_t lane16, uint32_t lds_addr) {
+  uint32_t voff, h;
+  asm volatile(
+      "v_and_b32 %0, 0x1f0, %2\n\t"            // 16 (l % 32)
+      "v_bfe_u32 %1, %2, 9, 1\n\t"              // l / 32
+      "v_mad_u32_u24 %0, %1, %3, %0\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %5"
+      : "=&v"(voff), "=&v"(h)
+      : "v"(lane16), "s"(hi_off), "s"(lds_addr), "s"(base)
+      : "memory");
+}
+__device__ __forceinline__ void dma8_rope(const void* base, int n0, int nlast, uint32_t rb, uint32_t lds_addr) {
+  uint32_t l, n;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 %0, -1, %0\n\t"       // l = lane id
+      "v_lshrrev_b32 %1, 4, %0\n\t"
+      "v_add_u32 %1, %2, %1\n\t"                // n = n0 + l/16
+      "v_min_i32 %1, %3, %1\n\t"
+      "v_and_b32 %0, 15, %0\n\t"
+      "v_lshlrev_b32 %0, 2, %0\n\t"             // 4 (l % 16)
+      "v_mad_u32_u24 %1, %1, %4, %0\n\t"        // nn*rb + 4 (l % 16) (nn < 32, rb < 2^24)
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %6"
+      : "=&v"(l), "=&v"(n)
+      : "s"(n0), "s"(nlast), "s"(rb), "s"(lds_addr), "s"(base)
+      : "memory");
+}
+
+// Eight E4M3 values (two dwords, lowest byte first) widened to the 16-bit
+// type DT: v_cvt_pk_f32_fp8 decodes two bytes to fp32 (exactly; the E4M3
+// NaN codes give NaN), and the pair is packed (exactly, as every E4M3 value
+// is representable in both 16-bit types).
+template <int DT>
+__device__ __forceinline__ uint32_t widen2(uint32_t w, bool hi) {
+  const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  return pack2<DT>(f.x, f.y);
+}
+
 // sbase + (lane_bits ^ key): per-tile LDS read addresses (sbase = the tile's
 // slot, lane_bits = this lane's loop-invariant offset bits, key = the part
 // that varies with the operand).  asm volatile keeps the compiler from
@@ -603,6 +663,48 @@ __device__ __forceinline__ void issue_part(const DmaCursor& c, const DmaTile& d,
   }
 }
 
+// This wave's part of an FP8 tile load into a staging slot: parts 0..3 the
+// latent rows 8w + 2 part, + 1 (staged row n at 512 n), parts 4 and 5 the RoPE
+// rows 8w + 4 (part - 4) .. + 3 (staged row n at kLat8Bytes + 64 n).  Rows
+// past nlast re-read row nlast.
+__device__ __forceinline__ void issue_part8(const DmaCursor& c, const DmaTile& d, int wave, uint32_t lane16,
+                                            int part) {
+  if (part < 4) {
+    const int n = 8 * wave + 2 * part;
+    const int nn = n < d.nlast ? n : d.nlast;
+    const uint32_t hi = n + 1 <= d.nlast ? c.lat_rb : 0u;
+    dma8_lat(d.lat + (uint32_t)nn * c.lat_rb, hi, lane16, d.lds + 1024 * (4 * wave + part));
+  } else {
+    const int j = part - 4;
+    dma8_rope(d.rope, 8 * wave + 4 * j, d.nlast, c.rope_rb, d.lds + kLat8Bytes + 256 * (2 * wave + j));
+  }
+}
+
+// Widening of an FP8 tile, this wave's share: the bytes its own loads
+// staged (so only its own load counter guards them, no barrier).  Nine
+// 16-byte chunks of the 16-bit ring slot per lane: for u = 0..3 the staged
+// 16 bytes at 1024 (4w + u) + 16 l, i.e. values 16 (l % 32) .. + 15 of latent
+// row n = 8w + 2u + l/32, become chunks 2 (l % 32) and 2 (l % 32) + 1 of that
+// row; then the staged RoPE bytes at kLat8Bytes + 512 w + 8 l, values
+// 8 (l % 8) .. + 7 of RoPE row 8w + l/8, become that row's chunk l % 8.
+// Ring positions follow the swizzles above, split into a per-lane part and a
+// wave-uniform key (disjoint bits, so xor and add agree):
+//   latent chunk 2 (l % 32) + e of row n: 8192 w + 2048 u + (lat8_lane ^ 16 k),
+//     lat8_lane = 1024 (l/32) + 16 (2 (l % 32) ^ 4 (l/32)),
+//     k = 8 (u % 2) ^ ((2w + u/2) % 4) ^ e;
+//   RoPE chunk l % 8 of row 8w + l/8: kLatBytes + 1024 w + (rope8_lane ^ 64 (w % 2)),
+//     rope8_lane = 128 (l/8) + 16 ((l % 8) ^ (l/16)).
+__device__ __forceinline__ uint32_t lat8_lane(uint32_t lane) {
+  const uint32_t h = lane >> 5;
+  return 1024u * h + 16u * ((2u * (lane & 31u)) ^ (4u * h));
+}
+__device__ __forceinline__ uint32_t rope8_lane(uint32_t lane) {
+  return 128u * (lane >> 3) + 16u * ((lane & 7u) ^ (lane >> 4));
+}
+__device__ __forceinline__ uint32_t lat8_key(int wave, int u, int e) {
+  return 16u * (uint32_t)((8 * (u & 1)) ^ ((2 * wave + (u >> 1)) & 3) ^ e);
+}
+
 
 // Softmax of one score tile, cut into steps so that the loop can run them one
 // or two instructions at a time between MFMAs.  x[] holds the raw scores
@@ -694,9 +796,10 @@ constexpr int kSoftmaxSteps = 23;
 //   drain      softmax of tile n-1 (masked), P·V of tile n-1.
 // Two tiles stay in flight, one barrier per tile; only the last tile can be
 // partial, so masking is confined to the drain.
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, bool KV8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitParams p) {
+  constexpr int EB = KV8 ? 1 : 2;   // bytes per cache element
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kTileBytes + kQLdsBytes];
   lds_char* lds = (lds_char*)lds_raw;
   lds_char* qlds = lds + kStages * kTileBytes;
@@ -796,22 +899,22 @@ void split_kernel(SplitParams p) {
   const uint32_t qwave = lds_u32(qlds) + 1024u * (uint32_t)wave;
 
   DmaCursor cur;
-  cur.lat_rb = (uint32_t)(p.kv_sr * 2);
-  cur.rope_rb = (uint32_t)(p.kpe_sr * 2);
+  cur.lat_rb = (uint32_t)(p.kv_sr * EB);
+  cur.rope_rb = (uint32_t)(p.kpe_sr * EB);
   cur.row = r0;
   if constexpr (PAGED) {
     cur.lat = reinterpret_cast<const char*>(p.kv);
     cur.rope = reinterpret_cast<const char*>(p.kpe);
     const int slot0 = r0 / p.page_size;
     cur.bt = (const_i32_ptr)(p.block_table + (int64_t)b * p.bt_stride + slot0);
-    cur.lat_pb = p.kv_sb * 2;
-    cur.rope_pb = p.kpe_sb * 2;
+    cur.lat_pb = p.kv_sb * EB;
+    cur.rope_pb = p.kpe_sb * EB;
     cur.page_size = p.page_size;
     cur.num_pages = p.num_pages;
     cur.in_page = r0 - slot0 * p.page_size;
   } else {
-    cur.lat = reinterpret_cast<const char*>(p.kv + (int64_t)b * p.kv_sb) + (int64_t)r0 * cur.lat_rb;
-    cur.rope = reinterpret_cast<const char*>(p.kpe + (int64_t)b * p.kpe_sb) + (int64_t)r0 * cur.rope_rb;
+    cur.lat = reinterpret_cast<const char*>(p.kv) + (int64_t)b * p.kv_sb * EB + (int64_t)r0 * cur.lat_rb;
+    cur.rope = reinterpret_cast<const char*>(p.kpe) + (int64_t)b * p.kpe_sb * EB + (int64_t)r0 * cur.rope_rb;
   }
 
   // LDS byte offsets inside a tile, as loop-invariant lane bits plus a key
@@ -833,7 +936,13 @@ void split_kernel(SplitParams p) {
     const int z = (G >> 1) & 3;
     vofs0 = 4096 * (G >> 1) + 1024 * (i >> 2) + 64 * (i >> 2) + 16 * (y ^ z) + 8 * (i & 1);
   }
-  auto slot = [&](int t) __attribute__((always_inline)) -> lds_char* { return lds + (t & (kStages - 1)) * kTileBytes; };
+  // Ring slot of tile t (16-bit operands), and with an FP8 cache the staging
+  // slot its bytes arrive in.
+  auto slot = [&](int t) __attribute__((always_inline)) -> lds_char* {
+    if constexpr (KV8) return lds + (t % kStages8) * kTileBytes;
+    return lds + (t & (kStages - 1)) * kTileBytes;
+  };
+  auto stage8 = [&](int t) __attribute__((always_inline)) -> lds_char* { return lds + kStaging8 + (t & 1) * kTile8Bytes; };
 
   const float c = p.scale_log2;
 
@@ -876,7 +985,7 @@ void split_kernel(SplitParams p) {
     qd.lat = reinterpret_cast<const char*>(p.q_nope + (int64_t)b * p.q_nope_sb + (int64_t)h0 * p.q_nope_sh);
     qd.rope = reinterpret_cast<const char*>(p.q_pe + (int64_t)b * p.q_pe_sb + (int64_t)h0 * p.q_pe_sh);
     qd.nlast = min(31, p.heads - 1 - h0);
-    qd.lds = lds_u32(slot(wave));
+    qd.lds = lds_u32(lds + wave * kTileBytes);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll
@@ -895,34 +1004,107 @@ void split_kernel(SplitParams p) {
   }
   __syncthreads();
 
-  // A wave whose 32 heads all lie past the last head (few heads per group)
-  // computes nothing: it only issues its share of every tile's loads and
-  // passes the same barriers as the other waves (prologue; one per step; the
-  // one before the epilogue), then leaves.  Wave 0 always has heads.
-  if (h0 >= p.heads) {
+  // FP8 cache: this wave's loads of tile t into its staging slot, and the
+  // pieces of widening a staged tile into its ring slot (see issue_part8 and
+  // lat8_lane): w8_read fetches staged group u (0..3 latent, 4 RoPE), w8_half
+  // widens half h of chunk c (c = 2u + e for latent, 8 for RoPE) and with
+  // h = 1 writes the chunk.  Two latent groups are held at a time.
+  u32x4 cx[2], cw;
+  u32x2 cy;
+  auto load8 = [&](int t, int pg) __attribute__((always_inline)) {
+    const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, stage8(t));
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      const int pg = PAGED ? cursor_page(cur) : 0;
-      const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(kk));
-#pragma unroll
-      for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
-      cursor_next<PAGED>(cur, r1);
+    for (int part = 0; part < kLoadsPerTile8; ++part) issue_part8(cur, d, wave, lane16, part);
+    cursor_next<PAGED>(cur, r1);
+  };
+  auto w8_read = [&](const lds_char* src, int u) __attribute__((always_inline)) {
+    if (u < 4) cx[u & 1] = lds_get16(src, 4096 * wave + 1024 * u + (int)lane16);
+    else cy = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(src + kLat8Bytes + 512 * wave + 8 * lane);
+  };
+  auto w8_half = [&](const lds_char* dst, int c, int h) __attribute__((always_inline)) {
+    const uint32_t a = c < 8 ? cx[(c >> 1) & 1][2 * (c & 1) + h] : (h ? cy.y : cy.x);
+    cw[2 * h] = widen2<DT>(a, false);
+    cw[2 * h + 1] = widen2<DT>(a, true);
+    if (h == 1) {
+      const uint32_t addr =
+          c < 8 ? xor_add(lds_u32(dst) + 8192u * wave + 2048u * (c >> 1), lat8_key(wave, c >> 1, c & 1), lat8_lane(lane))
+                : xor_add(lds_u32(dst) + kLatBytes + 1024u * wave, 64u * (wave & 1), rope8_lane(lane));
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((lds_char*)(uintptr_t)addr) = cw;
     }
-    wait_cnt<2 * kLoadsPerTile, 15>();
+  };
+  // A whole staged tile at once (prologue, idle waves).
+  auto widen_all = [&](const lds_char* src, const lds_char* dst) __attribute__((always_inline)) {
+    w8_read(src, 0);
+    w8_read(src, 1);
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      w8_half(dst, c, 0);
+      w8_half(dst, c, 1);
+      if (c == 1) w8_read(src, 2);
+      if (c == 3) w8_read(src, 3);
+      if (c == 5) w8_read(src, 4);
+    }
+  };
+  // FP8 prologue: tiles 0 and 1 staged and widened into ring slots 0 and 1,
+  // tiles 2 and 3 in flight into the staging slots (each issued once its
+  // slot's bytes have been widened); every wave's widening done at the
+  // barrier.
+  auto prologue8 = [&]() __attribute__((always_inline)) {
+    load8(0, PAGED ? cursor_page(cur) : 0);
+    load8(1, PAGED ? cursor_page(cur) : 0);
+    wait_cnt<kLoadsPerTile8, 15>();
+    widen_all(stage8(0), slot(0));
+    load8(2, PAGED ? cursor_page(cur) : 0);
+    wait_cnt<kLoadsPerTile8, 15>();
+    widen_all(stage8(1), slot(1));
+    load8(3, PAGED ? cursor_page(cur) : 0);
+    wait_cnt<63, 0>();
     barrier();
+  };
+
+  // A wave whose 32 heads all lie past the last head (few heads per group)
+  // computes nothing: it only issues its share of every tile's loads (and
+  // with an FP8 cache widens what it loaded) and passes the same barriers as
+  // the other waves (prologue; one per step; the one before the epilogue),
+  // then leaves.  Wave 0 always has heads.
+  if (h0 >= p.heads) {
+    if constexpr (KV8) {
+      prologue8();
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        const int pg = PAGED ? cursor_page(cur) : 0;
+        const DmaTile d = cursor_tile<PAGED>(cur, pg, r1, slot(kk));
+#pragma unroll
+        for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+        cursor_next<PAGED>(cur, r1);
+      }
+      wait_cnt<2 * kLoadsPerTile, 15>();
+      barrier();
+    }
     int pg_next = 0;
     if (n_tiles > 1) {
       if constexpr (PAGED) pg_next = cursor_page(cur);
-      wait_cnt<kLoadsPerTile, 0>();
+      if constexpr (KV8) wait_cnt<63, 0>();
+      else wait_cnt<kLoadsPerTile, 0>();
       barrier();
     }
     for (int t = 1; t < n_tiles; ++t) {
-      const DmaTile d = cursor_tile<PAGED>(cur, pg_next, r1, slot(t + 2));
-      cursor_next<PAGED>(cur, r1);
+      if constexpr (KV8) {
+        // step t: tile t+1 widened, tile t+3 loaded into its staging slot
+        wait_cnt<kLoadsPerTile8, 15>();
+        widen_all(stage8(t + 1), slot(t + 1));
+        load8(t + 3, pg_next);
+        if constexpr (PAGED) pg_next = cursor_page(cur);
+        wait_cnt<63, 0>();
+      } else {
+        const DmaTile d = cursor_tile<PAGED>(cur, pg_next, r1, slot(t + 2));
+        cursor_next<PAGED>(cur, r1);
 #pragma unroll
-      for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
-      if constexpr (PAGED) pg_next = cursor_page(cur);
-      wait_cnt<kLoadsPerTile, 0>();
+        for (int part = 0; part < kLoadsPerTile; ++part) issue_part(cur, d, wave, lane16, part);
+        if constexpr (PAGED) pg_next = cursor_page(cur);
+        wait_cnt<kLoadsPerTile, 0>();
+      }
       barrier();
     }
     wait_cnt<0, 15>();
@@ -940,9 +1122,11 @@ void split_kernel(SplitParams p) {
 
   {
     // ---- prologue ----------------------------------------------------------
-    {
-      // Always three tiles (the last one again past the end), so that every
-      // wait below counts the same loads.
+    // Always three tiles (FP8: four; the last one again past the end), so
+    // that every wait below counts the same loads.
+    if constexpr (KV8) {
+      prologue8();
+    } else {
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int pg = PAGED ? cursor_page(cur) : 0;
@@ -1070,18 +1254,45 @@ void split_kernel(SplitParams p) {
     // so loads issued in a burst stall the MFMAs behind them.  (Loads placed
     // between the score MFMAs, whose accumulator is in VGPRs, stalled longer
     // still.)
-    auto pv_range = [&](int i0, int i1, bool with_dma, int dma_t, int dma_pg) __attribute__((always_inline)) {
+    // FP8 cache: WITH_DMA also widens tile w_t (staged, into its ring slot)
+    // between the MFMAs, half a chunk per MFMA, each staged group read a few
+    // MFMAs ahead; after MFMA 0 the wave waits for its own loads of that
+    // tile (those of the next tile may still be in flight).  The 6 loads of
+    // tile dma_t go into the staging slot just widened, each once the group
+    // it overwrites has been read (its chunks written).
+    auto pv_range = [&](int i0, int i1, bool with_dma, int dma_t, int dma_pg, int w_t) __attribute__((always_inline)) {
       DmaTile dt{};
       if (i0 == 0 && with_dma) {
-        dt = cursor_tile<PAGED>(cur, dma_pg, r1, slot(dma_t));
+        dt = cursor_tile<PAGED>(cur, dma_pg, r1, KV8 ? stage8(dma_t) : slot(dma_t));
         cursor_next<PAGED>(cur, r1);
       }
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         if (i >= i0 && i < i1) {
           mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pk[i & 1]);
-          // A load right behind an MFMA, its issue stall overlapping the MFMA.
-          if (i0 == 0 && with_dma && i % 3 == 1 && i / 3 < kLoadsPerTile) issue_part(cur, dt, wave, lane16, i / 3);
+          if (i0 == 0 && with_dma) {
+            if constexpr (KV8) {
+              const lds_char* src = stage8(w_t);
+              const lds_char* dst = slot(w_t);
+              if (i == 0) {
+                wait_cnt<kLoadsPerTile8, 15>();
+                w8_read(src, 0);
+                w8_read(src, 1);
+              }
+              if (i >= 2 && i < 20) w8_half(dst, (i - 2) >> 1, i & 1);
+              if (i == 5) w8_read(src, 2);
+              if (i == 9) w8_read(src, 3);
+              if (i == 13) w8_read(src, 4);
+              // loads: part 0 after group 0 is written (i = 5), ... part 4, 5 after the RoPE (i = 19)
+              constexpr int kAt[kLoadsPerTile8] = {7, 11, 15, 17, 19, 21};
+#pragma unroll
+              for (int q = 0; q < kLoadsPerTile8; ++q)
+                if (i == kAt[q]) issue_part8(cur, dt, wave, lane16, q);
+            } else if (i % 3 == 1 && i / 3 < kLoadsPerTile) {
+              // A load right behind an MFMA, its issue stall overlapping the MFMA.
+              issue_part(cur, dt, wave, lane16, i / 3);
+            }
+          }
           if constexpr (DT == MLA_DTYPE_BF16) mfma_a<DT>(acc[i >> 1], vbuf[i % kVB], sm.pl[i & 1]);
           if (i + kVA < 32) vbuf[(i + kVA) % kVB] = v_read(i + kVA);
           fence();
@@ -1095,7 +1306,10 @@ void split_kernel(SplitParams p) {
     auto advance = [&](int t) __attribute__((always_inline)) -> int {
       int pg = 0;
       if constexpr (PAGED) pg = cursor_page(cur);   // the cursor is at tile t+3 (or the last)
-      wait_cnt<kLoadsPerTile, 0>();
+      // FP8: tile t+1 was widened in this step (its loads waited for there);
+      // the LDS counter covers the widened chunks.
+      if constexpr (KV8) wait_cnt<63, 0>();
+      else wait_cnt<kLoadsPerTile, 0>();
       barrier();
       k_head(slot(t + 1));
       fence();
@@ -1119,9 +1333,9 @@ void split_kernel(SplitParams p) {
     auto step = [&](int t, f32x16& cur, f32x16& prev) __attribute__((always_inline)) {
       phase_a(slot(t), cur, prev, true, t == 1, slot(t - 1));
       nops_before_mfma<DT>(sm.pk, sm.pl);
-      pv_range(0, 32 - kVA, true, t + 2, pg_next);
+      pv_range(0, 32 - kVA, true, KV8 ? t + 3 : t + 2, pg_next, t + 1);
       pg_next = advance(t);
-      pv_range(32 - kVA, 32, false, 0, 0);
+      pv_range(32 - kVA, 32, false, 0, 0, 0);
     };
     // The padding at the end of a trip: with the rescale branch in the loop,
     // the register allocator may swap accumulator tiles on the loop's exit
@@ -1160,7 +1374,7 @@ void split_kernel(SplitParams p) {
       for (int i = 0; i < kVA; ++i) vbuf[i] = v_read(i);
       nops_before_mfma<DT>(sm.pk, sm.pl);
       fence();
-      pv_range(0, 32, false, 0, 0);
+      pv_range(0, 32, false, 0, 0, 0);
     }
     // No load may still be writing the ring when the ending reuses it or the
     // workgroup leaves.
@@ -1179,7 +1393,9 @@ void split_kernel(SplitParams p) {
   const float ltot = halves_sum(lsum);
   const float lnorm = DT == MLA_DTYPE_F16 ? halves_sum(lsr) : ltot;
   const bool nonempty = ltot > 0.f;
-  const float inv = nonempty ? 1.f / lnorm : 0.f;
+  // FP8 cache: the products used the stored values; the scale multiplies
+  // the normalised output (and is already in c for the scores).
+  const float inv = nonempty ? (KV8 ? p.out_scale : 1.f) / lnorm : 0.f;
   const float lse2 = nonempty ? __log2f(ltot) - nmc : -__builtin_inff();
   if (s_b == 1 && head_ok_t && g_t == 0) p.lse[(int64_t)b * p.heads + h_t] = nonempty ? lse2 * kLn2 : -__builtin_inff();
   // The rows leave through LDS: each wave stages its 32 head rows in a
@@ -1728,15 +1944,22 @@ static void launch_k(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, h
   else hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
 }
 
-hipError_t launch_split(const SplitParams& p, int dtype, bool paged, int grid_x, int grid_y, hipStream_t stream,
-                        hipEvent_t t0, hipEvent_t t1) {
-  const dim3 grid(grid_x, grid_y), block(kThreads);
+template <int DT, bool KV8>
+static void launch_split_dt(const SplitParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t t0,
+                            hipEvent_t t1) {
+  if (paged) launch_k(split_kernel<DT, true, KV8>, grid, dim3(kThreads), stream, t0, t1, p);
+  else launch_k(split_kernel<DT, false, KV8>, grid, dim3(kThreads), stream, t0, t1, p);
+}
+
+hipError_t launch_split(const SplitParams& p, int dtype, bool paged, bool kv8, int grid_x, int grid_y,
+                        hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(grid_x, grid_y);
   if (dtype == MLA_DTYPE_F16) {
-    if (paged) launch_k(split_kernel<MLA_DTYPE_F16, true>, grid, block, stream, t0, t1, p);
-    else launch_k(split_kernel<MLA_DTYPE_F16, false>, grid, block, stream, t0, t1, p);
+    if (kv8) launch_split_dt<MLA_DTYPE_F16, true>(p, paged, grid, stream, t0, t1);
+    else launch_split_dt<MLA_DTYPE_F16, false>(p, paged, grid, stream, t0, t1);
   } else {
-    if (paged) launch_k(split_kernel<MLA_DTYPE_BF16, true>, grid, block, stream, t0, t1, p);
-    else launch_k(split_kernel<MLA_DTYPE_BF16, false>, grid, block, stream, t0, t1, p);
+    if (kv8) launch_split_dt<MLA_DTYPE_BF16, true>(p, paged, grid, stream, t0, t1);
+    else launch_split_dt<MLA_DTYPE_BF16, false>(p, paged, grid, stream, t0, t1);
   }
   return hipGetLastError();
 }

@@ -54,6 +54,23 @@ typedef enum mla_dtype {
   MLA_DTYPE_BF16 = 1          /* bfloat16 for q, cache and out                   */
 } mla_dtype;
 
+/*
+ * Storage of the KV cache (mla_desc.kv_dtype).  The TileLang MLA guide lists
+ * an FP8 KV-cache variant among its kernels ("变体内核",
+ * example_mla_decode_kv_fp8) without fixing the format; this library reads it
+ * as OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN; largest finite value 448; PyTorch's
+ * float8_e4m3fn) with one fp32 scale for the whole cache: a stored byte x
+ * stands for the value decode(x) * kv_scale.  Queries and output keep
+ * `dtype`; the products run on `dtype` MFMAs with the decoded bytes, which
+ * both 16-bit types hold exactly, and kv_scale multiplies the scores and the
+ * output.
+ */
+typedef enum mla_kv_dtype {
+  MLA_KV_AS_DTYPE = 0,        /* the cache holds `dtype` values                  */
+  MLA_KV_FP8_E4M3 = 1         /* the cache holds E4M3 bytes (see above)          */
+} mla_kv_dtype;
+
 /* Latent (value) width and RoPE width; the only supported sizes. */
 #define MLA_D_LATENT 512
 #define MLA_D_ROPE 64
@@ -67,10 +84,11 @@ typedef enum mla_dtype {
 #define MLA_MAX_ROW_STRIDE (1 << 22)
 
 /*
- * Problem description.  All strides are in ELEMENTS of the input dtype and must
- * keep every row start 16-byte aligned (multiples of 8 elements); kv_sr,
- * kpe_sr, q_nope_sh and q_pe_sh must be below MLA_MAX_ROW_STRIDE
- * (MLA_ERR_UNSUPPORTED otherwise).
+ * Problem description.  All strides are in ELEMENTS (of the input dtype; of
+ * the cache's storage for the cache strides, bytes with an FP8 cache) and must
+ * keep every row start 16-byte aligned (multiples of 8 elements, 16 bytes for
+ * an FP8 cache); kv_sr, kpe_sr, q_nope_sh and q_pe_sh must be below
+ * MLA_MAX_ROW_STRIDE (MLA_ERR_UNSUPPORTED otherwise).
  *
  * Contiguous cache (block_table == NULL):
  *   kv_latent[b, j, 0, :] at kv_latent + b*kv_sb + j*kv_sr      (512 values)
@@ -111,6 +129,12 @@ typedef struct mla_desc {
   int64_t kv_sb, kv_sr;          /* latent: batch (or page) stride, row stride   */
   int64_t kpe_sb, kpe_sr;        /* rope:   batch (or page) stride, row stride   */
   int64_t out_sb, out_sh;        /* out[b,h,:]     at out + b*sb + h*sh          */
+  /* Appended fields (a zero-filled struct keeps the 16-bit behaviour):      */
+  int32_t kv_dtype;              /* mla_kv_dtype of kv_latent and k_pe          */
+  float kv_scale;                /* FP8 cache: finite and > 0, value =
+                                    decode(byte) * kv_scale.  A 16-bit cache:
+                                    0 or 1 (anything else is
+                                    MLA_ERR_INVALID_ARG)                        */
 } mla_desc;
 
 /*

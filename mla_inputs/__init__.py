@@ -91,8 +91,11 @@ def f32_to_e4m3_bits(x: np.ndarray, kv_scale: float) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
-def _normal_rows(seed_seq: np.random.SeedSequence, n_rows: int, width: int, dtype: str) -> np.ndarray:
-    """``n_rows x width`` N(0,1) values in storage format, filled chunk-wise in parallel."""
+def _normal_rows(seed_seq: np.random.SeedSequence, n_rows: int, width: int, dtype: str,
+                 kv_scale: Optional[float] = None) -> np.ndarray:
+    """``n_rows x width`` N(0,1) values in storage format, filled chunk-wise in
+    parallel.  ``dtype="fp8"``: the values drawn as for fp16, then quantised
+    to E4M3 bytes of value / kv_scale."""
     out = np.empty((n_rows, width), dtype=storage_np_dtype(dtype))
     n_chunks = (n_rows + _CHUNK_ROWS - 1) // _CHUNK_ROWS
     children = seed_seq.spawn(n_chunks)
@@ -101,7 +104,11 @@ def _normal_rows(seed_seq: np.random.SeedSequence, n_rows: int, width: int, dtyp
         r0 = i * _CHUNK_ROWS
         r1 = min(n_rows, r0 + _CHUNK_ROWS)
         g = np.random.default_rng(children[i])
-        out[r0:r1] = cast_storage(g.standard_normal((r1 - r0, width), dtype=np.float32), dtype)
+        x = g.standard_normal((r1 - r0, width), dtype=np.float32)
+        if dtype == "fp8":
+            out[r0:r1] = f32_to_e4m3_bits(cast_storage(x, "f16").astype(np.float32), kv_scale)
+        else:
+            out[r0:r1] = cast_storage(x, dtype)
 
     if n_chunks <= 1:
         for i in range(n_chunks):
@@ -168,7 +175,7 @@ def _cache_rows(seed_seq, n_rows: int, dtype: str, kv_dtype: str, kv_scale: floa
     bytes of value / kv_scale."""
     if kv_dtype != "fp8":
         return _normal_rows(seed_seq, n_rows, D_QK, dtype)
-    return f32_to_e4m3_bits(_normal_rows(seed_seq, n_rows, D_QK, "f16").astype(np.float32), kv_scale)
+    return _normal_rows(seed_seq, n_rows, D_QK, "fp8", kv_scale)
 
 
 def _kv_args(kv_dtype, kv_scale):
@@ -304,10 +311,13 @@ CONFIG_NAMES = {
 
 
 def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1,
-                heads: Optional[int] = None) -> MlaInputs:
+                heads: Optional[int] = None, kv_dtype: Optional[str] = None) -> MlaInputs:
     """Build workload ``idx`` (0..4).  ``batch_subset`` keeps only the first sequences;
     ``seqlen_q`` > 1 gives every sequence that many query tokens (of H heads each);
-    ``heads`` replaces H (e.g. one tensor-parallel shard's heads).
+    ``heads`` replaces H (e.g. one tensor-parallel shard's heads); ``kv_dtype="fp8"``
+    stores the same N(0,1) cache rows as E4M3 bytes with DEFAULT_KV_SCALE (configs
+    0..3; the stress pattern's x8 rows would saturate E4M3), named with a
+    ``_kvfp8`` suffix.
 
     0: B=2, H=16, L=256, fp16, contiguous.
     1: B=64, H=128, L=4096, fp16, contiguous.
@@ -316,6 +326,10 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1,
     4: B=2, H=128, L=131072, bf16, paged (64), shuffled, 1% of rows x8.
     """
     Hx = heads
+    fp8 = kv_dtype == "fp8"
+    if fp8 and idx == 4:
+        raise ValueError("the stress workload scales rows x8, beyond what E4M3 at the default scale holds")
+    suffix = "_kvfp8" if fp8 else ""
     if idx == 0:
         B, H, L, dt = 2, 16, 256, "f16"
     elif idx == 1:
@@ -328,8 +342,9 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1,
         if batch_subset is not None:
             lens = lens[:batch_subset]
             B = batch_subset
-        inp = make_paged(B, H, lens, "bf16", seed=3, page_block_size=64, max_blocks=256, seqlen_q=seqlen_q)
-        inp.meta["config"] = CONFIG_NAMES[3]
+        inp = make_paged(B, H, lens, "bf16", seed=3, page_block_size=64, max_blocks=256, seqlen_q=seqlen_q,
+                         kv_dtype=kv_dtype)
+        inp.meta["config"] = CONFIG_NAMES[3] + suffix
         return inp
     elif idx == 4:
         B, H, L = 2, Hx or 128, 131072
@@ -344,6 +359,6 @@ def make_config(idx: int, batch_subset: Optional[int] = None, seqlen_q: int = 1,
     if batch_subset is not None:
         B = batch_subset
     H = Hx or H
-    inp = make_contiguous(B, H, L, [L] * B, dt, seed=idx, seqlen_q=seqlen_q)
-    inp.meta["config"] = CONFIG_NAMES[idx]
+    inp = make_contiguous(B, H, L, [L] * B, dt, seed=idx, seqlen_q=seqlen_q, kv_dtype=kv_dtype)
+    inp.meta["config"] = CONFIG_NAMES[idx] + suffix
     return inp

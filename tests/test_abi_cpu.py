@@ -144,6 +144,49 @@ def test_validation_errors(L, case, expect):
     assert L.mla_last_error().decode()
 
 
+@pytest.mark.parametrize("case,expect", [
+    ("kv_dtype", _lib.MLA_ERR_UNSUPPORTED),
+    ("fp8_zero_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("fp8_neg_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("fp8_inf_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("fp8_nan_scale", _lib.MLA_ERR_INVALID_ARG),
+    ("fp8_row_stride_not_16", _lib.MLA_ERR_UNSUPPORTED),
+    ("fp8_page_stride_not_16", _lib.MLA_ERR_UNSUPPORTED),
+    ("scale_on_16bit_cache", _lib.MLA_ERR_INVALID_ARG),
+])
+def test_kv_cache_format_validation(L, case, expect):
+    """An FP8 cache needs a finite positive kv_scale and cache strides in
+    multiples of 16 bytes (rows 16-byte aligned); a 16-bit cache takes no
+    scale (0 and 1 mean none); other kv_dtype values are unsupported."""
+    d = _desc(kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=0.5)
+    kw = {}
+    if case == "kv_dtype":
+        d.kv_dtype = 2
+    elif case == "fp8_zero_scale":
+        d.kv_scale = 0.0
+    elif case == "fp8_neg_scale":
+        d.kv_scale = -0.5
+    elif case == "fp8_inf_scale":
+        d.kv_scale = float("inf")
+    elif case == "fp8_nan_scale":
+        d.kv_scale = float("nan")
+    elif case == "fp8_row_stride_not_16":
+        d.kv_sr = 520   # a multiple of 8 (fine for a 16-bit cache), not of 16 bytes
+    elif case == "fp8_page_stride_not_16":
+        d.page_block_size, d.block_table_stride, d.num_pages = 64, 4, 8
+        d.kv_sb, d.kv_sr, d.kpe_sb, d.kpe_sr = 64 * 576 + 8, 576, 64 * 576, 576
+        kw["block_table"] = FAKE
+    elif case == "scale_on_16bit_cache":
+        d.kv_dtype, d.kv_scale = _lib.MLA_KV_AS_DTYPE, 0.5
+    st = _decode(L, d, **kw)
+    assert st == expect, (case, st, L.mla_last_error())
+    assert L.mla_last_error().decode()
+    # the same description with a good scale and 16-byte strides passes validation (MLA_ERR_WORKSPACE:
+    # the fake workspace size is checked after every argument)
+    good = _desc(kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=0.5)
+    assert _decode(L, good, ws=None, ws_bytes=0) in (_lib.MLA_ERR_WORKSPACE, _lib.MLA_ERR_HIP)
+
+
 def test_empty_batch_is_ok_without_touching_memory(L):
     d = _desc(B=0)
     assert _decode(L, d, ptrs={k: None for k in ("q", "qp", "kv", "kpe", "lens", "out", "lse")}) == _lib.MLA_OK

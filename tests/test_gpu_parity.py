@@ -30,7 +30,7 @@ def _run(mla, inp, num_split, dev=None):
     from mla_inputs.torch_io import from_device, to_device
     d = dev or to_device(inp, "cuda")
     out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"],
-                              d["cache_seqlens"], inp.softmax_scale, num_split=num_split)
+                              d["cache_seqlens"], inp.softmax_scale, num_split=num_split, kv_scale=d["kv_scale"])
     torch.cuda.synchronize()
     return from_device(out), from_device(lse)
 
@@ -558,11 +558,12 @@ def _run_tokens(mla, inp, num_split):
     # A fresh workspace of NaN bytes: a split slot the kernels never wrote
     # would turn into NaN output instead of reusing an earlier call's partial.
     probe = torch.empty((B, s * H, 512), dtype=d["q_nope"].dtype, device="cuda")
-    desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], probe, seqlen_q=s)
+    desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], probe, seqlen_q=s,
+                         kv_scale=d["kv_scale"])
     ws = torch.full((mla.mla_workspace_size(desc, num_split, mla.mla_num_cus(0)),), 0xFF, dtype=torch.uint8,
                     device="cuda")
     out, lse = mla.mla_decode(qn, qp, d["kv_latent"], d["k_pe"], d["block_table"], d["cache_seqlens"],
-                              inp.softmax_scale, num_split=num_split, workspace=ws)
+                              inp.softmax_scale, num_split=num_split, workspace=ws, kv_scale=d["kv_scale"])
     torch.cuda.synchronize()
     assert tuple(out.shape) == (B, s, H, 512) and tuple(lse.shape) == (B, s, H)
     return from_device(out).reshape(B, s * H, 512), from_device(lse).reshape(B, s * H)

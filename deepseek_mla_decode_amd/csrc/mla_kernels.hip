@@ -547,14 +547,23 @@ __device__ __forceinline__ void dma8_rope(const void* base, int n0, int nlast, u
       : "memory");
 }
 
-// Eight E4M3 values (two dwords, lowest byte first) widened to the 16-bit
-// type DT: v_cvt_pk_f32_fp8 decodes two bytes to fp32 (exactly; the E4M3
-// NaN codes give NaN), and the pair is packed (exactly, as every E4M3 value
-// is representable in both 16-bit types).
-template <int DT>
-__device__ __forceinline__ uint32_t widen2(uint32_t w, bool hi) {
-  const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  return pack2<DT>(f.x, f.y);
+// Two E4M3 values (the low or the high byte pair of w, lowest byte first)
+// widened to the 16-bit type DT in one instruction, v_cvt_scalef32_pk_*_fp8
+// with scale 1: exact, as every E4M3 value is an fp16 and a bf16 value, and
+// the E4M3 NaN codes give NaN.  Written as asm: the compiler's own lowering
+// of the builtin extracted the second half of the result wrongly (both
+// halves came out as the first byte's value).
+template <int DT, bool HI>
+__device__ __forceinline__ uint32_t widen2(uint32_t w) {
+  uint32_t r;
+  if constexpr (DT == MLA_DTYPE_F16) {
+    if constexpr (HI) asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+    else asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  } else {
+    if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+    else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  }
+  return r;
 }
 
 // sbase + (lane_bits ^ key): per-tile LDS read addresses (sbase = the tile's
@@ -567,14 +576,6 @@ __device__ __forceinline__ uint32_t xor_add(uint32_t sbase, uint32_t key, uint32
   return r;
 }
 
-// a ^ K as an opaque VALU op, formed where it is used: the compiler would
-// otherwise keep it in a register through the tile loop.
-template <uint32_t K>
-__device__ __forceinline__ uint32_t xor_imm(uint32_t a) {
-  uint32_t r;
-  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(K), "v"(a));
-  return r;
-}
 
 __device__ __forceinline__ const lds_char* lds_at(uint32_t addr) {
   return (const lds_char*)(uintptr_t)addr;
@@ -717,16 +718,19 @@ __device__ __forceinline__ uint32_t lat8_key(int wave, int u, int e) {
 // (log2 units): P = 2^(c x - c m) may exceed 1, which is exact while it stays
 // inside the range of the P·V operand type.  Step 5 leaves dn = c m - c
 // tmax (<= 0 when the tile's max is higher); raising m means scaling the
-// accumulator (all 256 AGPRs of the lane) and the running sums by alpha =
+// accumulator (all 256 AGPRs of the lane) and the running sum by alpha =
 // 2^dn, which the loop does in a rarely taken branch right after step 5,
 // before this tile's exponentials and sums.  Only nmc = -c m is kept.
 //
 // Two running sums of P: `lsum` of the fp32 values (it gives the split's
 // log-sum-exp, hence the weights between splits) and, for fp16, `lsr` of the
-// values as rounded for the P·V product.  The split's output is normalised by
-// lsr, so that it is exactly a convex combination of value rows under the
-// weights actually multiplied: the rounding of a dominant P then cancels.
-// bf16 keeps P as hi + lo (relative error 2^-17), so lsum serves both.
+// values as rounded for the P·V product (one v_dot2c per packed pair).  The
+// split's output is normalised by lsr, so that it is exactly a convex
+// combination of value rows under the weights actually multiplied: the
+// rounding of a dominant P then cancels.  (The lse from lsr too would carry
+// P's rounding, up to 2^-11 relative, into the weights between splits,
+// where large value rows of two splits that cancel amplify it.)  bf16 keeps
+// P as hi + lo (relative error 2^-17), so lsum serves both.
 template <int DT>
 constexpr float kRescaleMargin = DT == MLA_DTYPE_F16 ? 15.0f : 64.0f;
 
@@ -1023,8 +1027,8 @@ void split_kernel(SplitParams p) {
   };
   auto w8_half = [&](const lds_char* dst, int c, int h) __attribute__((always_inline)) {
     const uint32_t a = c < 8 ? cx[(c >> 1) & 1][2 * (c & 1) + h] : (h ? cy.y : cy.x);
-    cw[2 * h] = widen2<DT>(a, false);
-    cw[2 * h + 1] = widen2<DT>(a, true);
+    cw[2 * h] = widen2<DT, false>(a);
+    cw[2 * h + 1] = widen2<DT, true>(a);
     if (h == 1) {
       const uint32_t addr =
           c < 8 ? xor_add(lds_u32(dst) + 8192u * wave + 2048u * (c >> 1), lat8_key(wave, c >> 1, c & 1), lat8_lane(lane))
@@ -1147,7 +1151,7 @@ void split_kernel(SplitParams p) {
     constexpr int kVA = DT == MLA_DTYPE_F16 ? 3 : 2;
     constexpr int kKB = kKA + 1, kVB = kVA + 1;
     u32x4 kb[kKB], vbuf[kVB], qb[4];
-    uint32_t kq[8], vw[4];
+    uint32_t kq[8], vw[4], vw1[4];
     f32x16 sA, sB;
     Softmax<DT> sm;
 
@@ -1167,17 +1171,21 @@ void split_kernel(SplitParams p) {
     auto q_op = [&](int s) __attribute__((always_inline)) -> const u32x4& {
       return s < kQRegSteps ? qreg[s < kQRegSteps ? s : 0] : qb[s < kQRegSteps ? 0 : s - kQRegSteps];
     };
-    // Value-operand bases of a tile; operand i = 2 vb + kt, two reads.
+    // Value-operand bases of a tile; operand i = 2 vb + kt, two reads: half r
+    // = 1 is half 0 with bit 5 flipped (vofs1 above), kept in registers of
+    // its own (forming it at each read cost one VALU op per operand).
     auto v_bases = [&](const lds_char* tile) __attribute__((always_inline)) {
       const uint32_t base = lds_u32(tile);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) vw[cc] = xor_add(base, 64u * cc, vofs0);
+      for (int cc = 0; cc < 4; ++cc) {
+        vw[cc] = xor_add(base, 64u * cc, vofs0);
+        vw1[cc] = xor_add(base, 64u * cc + 32u, vofs0);
+      }
     };
     auto v_read = [&](int i) __attribute__((always_inline)) -> u32x4 {
       const int vb = i >> 1, kt = i & 1;
       const int imm = 256 * (vb >> 2) + 16384 * kt;
-      // Half r = 1 is half 0 with bit 5 flipped (the tile base is 1 KiB aligned).
-      return lds_get_tr(lds_at(vw[vb & 3]), imm, lds_at(xor_imm<32>(vw[vb & 3])), imm + 8192);
+      return lds_get_tr(lds_at(vw[vb & 3]), imm, lds_at(vw1[vb & 3]), imm + 8192);
     };
     // A tile whose max passed the reference by more than the margin (Softmax
     // step 5 leaves dn < -margin): raise the reference to that max and scale

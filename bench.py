@@ -56,22 +56,31 @@ def workload_figures(lens, heads: int, seqlen_q: int = 1, kv_elt: int = 2):
     return flops, kv_bytes, total_bytes
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or
-    None when there is none for this workload or the kernel source changed
-    since the counters were taken."""
+def measured_counters(workload: str):
+    """From the committed rocprofv3 summary of this workload (profiles/*.md):
+    HBM bytes per split-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain-copy calibration), the split kernel's MFMA-busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES)) and the file.
+    None for each when there is no summary for this workload or the kernel
+    source changed since the counters were taken."""
     import glob
     import hashlib
     src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+    traffic = busy = source = None
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(f):
-            if line.startswith("traffic-json:"):
-                rec = json.loads(line.split(":", 1)[1])
-                if rec.get("workload") == workload and rec.get("source_sha256") == sha:
-                    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
-    return None
+            for tag in ("traffic-json:", "counters-json:"):
+                if line.startswith(tag):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("workload") != workload or rec.get("source_sha256") != sha:
+                        continue
+                    source = os.path.relpath(f, ROOT)
+                    if tag == "traffic-json:":
+                        traffic = int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+                    else:
+                        busy = float(rec["mfma_busy"])
+    return traffic, busy, source
 
 
 def split_bounds(flops: float, total_bytes: float, split_ms: float, traffic):
@@ -253,7 +262,8 @@ def main() -> int:
     ai = flops / total_bytes
     roof_tflops = min(HBM_PEAK_GBS * 1e9 * ai / 1e12, MFMA_PEAK_TFLOPS)
     mean_L = float(np.mean(inp.cache_seqlens))
-    bounds = split_bounds(flops, total_bytes, split_avg, measured_traffic(workload))
+    traffic, mfma_busy, counter_file = measured_counters(workload)
+    bounds = split_bounds(flops, total_bytes, split_avg, traffic)
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -285,6 +295,9 @@ def main() -> int:
         # (several query tokens share each cache row); the other bound beside it.
         "roofline": bounds[0],
         "other_bound": bounds[1],
+        # Counter-measured share of the split kernel's cycles with the MFMA
+        # unit busy (the committed rocprofv3 summary of this workload).
+        "counters": {"mfma_busy": mfma_busy, "source": counter_file},
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 1),
     }

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "mla_decode", "mla_decode_noalloc", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
     "mla_num_cus", "mla_last_error", "mla_timing_enable", "mla_timing_read", "make_desc",
+    "mla_check_block_table",
     "MlaDesc", "MlaError",
 ]
 
@@ -308,6 +309,30 @@ def mla_plan_device(cache_seqlens, heads: int, num_split: int, num_cus: int, str
         cache_seqlens.data_ptr(), B, int(heads), int(seqlen_q), int(num_split), int(num_cus), ns.data_ptr(),
         off.data_ptr(), work.data_ptr(), int(max_work), s.cuda_stream))
     return ns, off, work
+
+
+def mla_check_block_table(block_table, cache_seqlens, num_pages: int, page_block_size: int, stream=None):
+    """Entries of a paged cache's block table that mla_decode reads (j <
+    ceil(L_b / page_block_size)) and that lie outside [0, num_pages), per
+    sequence: an int32 tensor [B] on the GPU.  mla_decode itself clamps such
+    entries into the pool (valid memory, wrong rows); this makes them
+    visible.  Enqueued on ``stream``; nothing synchronises."""
+    torch = _torch()
+    if not block_table.is_cuda:
+        raise ValueError("block_table must live on the GPU")
+    _check_placement(block_table, dict(cache_seqlens=cache_seqlens))
+    B = cache_seqlens.shape[0] if cache_seqlens.dim() == 1 else -1
+    _check_batch_arrays(B, cache_seqlens, block_table)
+    d = MlaDesc()
+    d.batch = B
+    d.page_block_size = int(page_block_size)
+    d.block_table_stride = block_table.stride(0)
+    d.num_pages = int(num_pages)
+    bad = torch.empty(max(B, 1), dtype=torch.int32, device=block_table.device)[:B]
+    s = torch.cuda.current_stream(block_table.device) if stream is None else stream
+    _lib.check(_lib.lib().mla_check_block_table(block_table.data_ptr(), cache_seqlens.data_ptr(), ctypes.byref(d),
+                                                bad.data_ptr(), s.cuda_stream))
+    return bad
 
 
 def mla_timing_enable(enable: bool = True) -> None:

@@ -71,6 +71,7 @@ SIGNATURES = {
                                   ctypes.POINTER(MlaDesc), _P, ctypes.c_size_t, _P]),
     "mla_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
                                           ctypes.POINTER(MlaDesc), _P]),
+    "mla_check_block_table": (ctypes.c_int, [_P, _P, ctypes.POINTER(MlaDesc), _P, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "mla_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _PI32]),

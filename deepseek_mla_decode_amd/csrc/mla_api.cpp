@@ -431,6 +431,32 @@ int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_late
                      d, nullptr, 0, true, stream);
 }
 
+int mla_check_block_table(const int32_t* block_table, const int32_t* cache_seqlens, const mla_desc* d,
+                          int32_t* bad, hipStream_t stream) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", d->batch);
+  if (d->batch == 0) return ok();
+  if (!block_table || !cache_seqlens || !bad) return fail(MLA_ERR_INVALID_ARG, "NULL array");
+  if (!aligned(block_table, 4) || !aligned(cache_seqlens, 4) || !aligned(bad, 4))
+    return fail(MLA_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
+  if (d->page_block_size < 32 || d->page_block_size % 32)
+    return fail(MLA_ERR_UNSUPPORTED, "page_block_size %d must be a positive multiple of 32", d->page_block_size);
+  if (d->block_table_stride < 1) return fail(MLA_ERR_INVALID_ARG, "block_table_stride < 1");
+  if (d->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages < 1");
+  mla::BlockCheckParams p{};
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.bad = bad;
+  p.page_size = d->page_block_size;
+  p.bt_stride = d->block_table_stride;
+  p.num_pages = d->num_pages;
+  const int64_t cap = (int64_t)d->block_table_stride * d->page_block_size;
+  p.row_cap = cap > INT32_MAX ? INT32_MAX : (int32_t)cap;
+  hipError_t e = mla::launch_check_block_table(p, d->batch, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "block-table check launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int mla_timing_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_timing = enable != 0;

@@ -59,7 +59,16 @@ struct PlanParams {
   int32_t row_cap;              // lengths are clamped to [0, row_cap]
 };
 
+struct BlockCheckParams {
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  int32_t* bad;                 // [B] out: entries read and outside [0, num_pages)
+  int32_t page_size, bt_stride, num_pages;
+  int32_t row_cap;              // lengths are clamped to [0, row_cap] (as in the split kernel)
+};
+
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_check_block_table(const BlockCheckParams& p, int batch, hipStream_t stream);
 // This device's no-allocation scratch array: its device address (taken once
 // per device with hipGetSymbolAddress) and size (MLA_NOALLOC_SCRATCH_BYTES).
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);

@@ -299,21 +299,31 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+// Sum of a 64-bit value over the lanes: three 16-bit slices summed with
+// wave_sum_i32 (each slice sum stays below 2^22 in 32 bits), recombined;
+// for the per-lane sums the planner forms (below 2^46).
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int lo = wave_sum_i32((int)(v & 0xFFFF));
+  const int mid = wave_sum_i32((int)((v >> 16) & 0xFFFF));
+  const int hi = wave_sum_i32((int)(v >> 32));
+  return ((int64_t)hi << 32) + ((int64_t)mid << 16) + (int64_t)lo;
+}
+// Inclusive prefix sum over the 64 lanes with DPP: within each row of 16
+// lanes by shifts of 1, 2, 4 and 8 (a lane shifted in from outside the row
+// adds 0), then across rows: row_bcast:15 adds the last lane of rows 0 and 2
+// to rows 1 and 3, row_bcast:31 adds lane 31 (rows 0 + 1) to rows 2 and 3.
+// Every lane must be active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2 and 3
   return v;
 }
-// Exclusive prefix sum over the lanes of a wave.
-__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  return inc - v;
-}
+// A value of lane `src` (wave-uniform) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 struct WorkItem {
   int b, k, r0, r1, s_b;
@@ -398,8 +408,9 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   }
   const int t = lo;
   const int mine = lane_splits(t) + tail * (b1 - b0);   // all splits of the lane's sequences
-  const int off = wave_excl_scan(mine, lane);
-  const int total = __shfl(off + mine, 63);
+  const int incl = wave_incl_scan(mine);
+  const int off = incl - mine;
+  const int total = lane_value(incl, 63);
   if (publish) {
     int o = off;
     for (int b = b0; b < b1; ++b) {
@@ -434,9 +445,9 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
   } else {
     j = wi - ntail;              // the j-th prefix split
     const int mine_pre = mine - tail * (b1 - b0);
-    const int off_pre = wave_excl_scan(mine_pre, lane);
+    const int off_pre = wave_incl_scan(mine_pre) - mine_pre;
     owner = __builtin_ctzll(__ballot(j >= off_pre && j < off_pre + mine_pre));
-    j -= __shfl(off_pre, owner);
+    j -= lane_value(off_pre, owner);
   }
   int fb = 0, fk = 0, fL = 0, fslot = 0;
   if (lane == owner) {
@@ -455,10 +466,10 @@ __device__ WorkItem plan_item(const SplitParams& p, int wi, int lane, bool publi
       o += spre + tail;
     }
   }
-  it.b = __shfl(fb, owner);
-  it.k = __shfl(fk, owner);
-  it.slot = __shfl(fslot, owner);
-  const int L = __shfl(fL, owner);
+  it.b = lane_value(fb, owner);
+  it.k = lane_value(fk, owner);
+  it.slot = lane_value(fslot, owner);
+  const int L = lane_value(fL, owner);
   const int spre = splits_for_budget(pre_blocks(L), t);
   it.s_b = spre + tail;
   seq_split_range(L, sq, spre, it.k, &it.r0, &it.r1);
@@ -1906,6 +1917,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Block-table check.  The split kernel clamps a page index outside
+// [0, num_pages) into the pool: it reads valid memory, but not the rows
+// meant.  This kernel (one workgroup per sequence) counts the entries the
+// split kernel reads, j < ceil(L_b / page_size) with L_b clamped as there,
+// that lie outside the pool: bad[b] for sequence b.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void check_block_table_kernel(BlockCheckParams p) {
+  __shared__ int red[256];
+  const int b = blockIdx.x;
+  const int L = clamp_len(p.seqlens[b], p.row_cap);
+  const int nblk = (L + p.page_size - 1) / p.page_size;
+  int bad = 0;
+  for (int j = threadIdx.x; j < nblk; j += 256) {
+    const int pg = p.block_table[(int64_t)b * p.bt_stride + j];
+    bad += (pg < 0 || pg >= p.num_pages) ? 1 : 0;
+  }
+  red[threadIdx.x] = bad;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.bad[b] = red[0];
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -1936,6 +1973,11 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
   *ptr = addr[dev];
   *bytes = MLA_NOALLOC_SCRATCH_BYTES;
   return hipSuccess;
+}
+
+hipError_t launch_check_block_table(const BlockCheckParams& p, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(check_block_table_kernel, dim3(batch), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {

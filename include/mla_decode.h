@@ -260,6 +260,25 @@ int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_late
                        const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
                        int32_t num_split, void* out, float* lse, const mla_desc* desc, hipStream_t stream);
 
+/*
+ * Block-table check (paged cache).  mla_decode reads block_table entries
+ * without checking them on the host (they are device memory): an entry it
+ * reads that lies outside [0, desc->num_pages) is clamped into the pool, so
+ * the call reads valid memory but rows other than the ones meant, and
+ * returns MLA_OK.  This call detects such tables: one small kernel counts,
+ * for each sequence b, the entries mla_decode would read (j <
+ * ceil(L_b / page_block_size), L_b clamped as mla_decode clamps it) that lie
+ * outside the pool, and writes the count to bad[b].  Entries past a
+ * sequence's length are not read and not counted.
+ *   block_table, cache_seqlens  as for mla_decode (device)
+ *   desc   batch, page_block_size, block_table_stride, num_pages are used
+ *   bad    device int32[batch] (out)
+ * Enqueued on `stream`; errors as for mla_decode (MLA_ERR_INVALID_ARG for
+ * NULL pointers or bad paging fields).
+ */
+int mla_check_block_table(const int32_t* block_table, const int32_t* cache_seqlens, const mla_desc* desc,
+                          int32_t* bad, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char* mla_last_error(void);
 

@@ -366,3 +366,22 @@ def test_combine_xcd_order_is_a_bijection_matching_the_split_order():
             b = (before(total, f % 8) + f // 8) // gx
             if len(split_xcd[b]) == 1:
                 assert f % 8 in split_xcd[b], (B, s, b)
+
+
+def test_block_table_check_validation(L):
+    """mla_check_block_table rejects a missing description, NULL arrays and
+    bad paging fields before launching anything; an empty batch is a no-op."""
+    d = _desc(B=2, page_block_size=64, block_table_stride=4, num_pages=8)
+    chk = lambda desc, bt=FAKE, lens=FAKE, bad=FAKE: L.mla_check_block_table(  # noqa: E731
+        bt, lens, None if desc is None else ctypes.byref(desc), bad, None)
+    assert chk(None) == _lib.MLA_ERR_INVALID_ARG
+    for kw in ({"bt": None}, {"lens": None}, {"bad": None}, {"bad": FAKE + 2}):
+        assert chk(d, **kw) == _lib.MLA_ERR_INVALID_ARG, kw
+    for field, value, want in (("page_block_size", 16, _lib.MLA_ERR_UNSUPPORTED),
+                               ("block_table_stride", 0, _lib.MLA_ERR_INVALID_ARG),
+                               ("num_pages", 0, _lib.MLA_ERR_INVALID_ARG), ("batch", -1, _lib.MLA_ERR_INVALID_ARG)):
+        bad_desc = _desc(B=2, page_block_size=64, block_table_stride=4, num_pages=8)
+        setattr(bad_desc, field, value)
+        assert chk(bad_desc) == want, field
+        assert L.mla_last_error().decode()
+    assert chk(_desc(B=0), bt=None, lens=None, bad=None) == _lib.MLA_OK

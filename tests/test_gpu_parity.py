@@ -732,3 +732,35 @@ def test_wide_partial_rows_over_a_stale_workspace(mla, dtype):
                               inp.softmax_scale, num_split=ns, out=out, workspace=ws)
         torch.cuda.synchronize()
         assert_parity(from_device(o), from_device(l), ro, rl, f"stale workspace {dtype} split={ns}")
+
+
+def test_block_table_check_counts_entries_read(mla):
+    """mla_check_block_table counts, per sequence, the block-table entries
+    mla_decode reads (j < ceil(L / page)) that lie outside the pool; entries
+    past a sequence's length are not read and not counted.  mla_decode itself
+    clamps such entries into the pool and stays finite."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    lens = [1, 64, 65, 300, 0]
+    inp = mi.make_paged(len(lens), 16, lens, "bf16", seed=150, page_block_size=64, spare_pages=2, max_blocks=8)
+    P = inp.pool.shape[0]
+    bt = inp.block_table.copy()
+    assert bt[4].max() < 0 and bt[0, 1] < 0          # unread entries hold -1
+    bt[1, 0] = P                                      # read (1 block): past the pool
+    bt[3, 2] = -7                                     # read (5 blocks)
+    bt[3, 4] = P + 100                                # read
+    bt[2, 5] = P + 1                                  # past ceil(65 / 64) = 2 blocks: not read
+    inp.block_table = bt
+    d = to_device(inp, "cuda")
+    bad = mla.mla_check_block_table(d["block_table"], d["cache_seqlens"], P, 64)
+    torch.cuda.synchronize()
+    assert bad.cpu().tolist() == [0, 1, 0, 2, 0]
+    good = mla.mla_check_block_table(to_device(mi.make_paged(len(lens), 16, lens, "bf16", seed=150,
+                                                            page_block_size=64, spare_pages=2,
+                                                            max_blocks=8), "cuda")["block_table"],
+                                     d["cache_seqlens"], P, 64)
+    assert good.cpu().tolist() == [0] * len(lens)
+    out, lse = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"],
+                              d["cache_seqlens"], inp.softmax_scale)
+    torch.cuda.synchronize()
+    assert np.isfinite(from_device(out)).all()

@@ -1768,7 +1768,14 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
   const int64_t stride = (int64_t)p.heads * 512;   // elements between consecutive splits
   const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
-  const float l0 = lse_value(lane_lse(L, p.heads, s, lane)), l1 = lse_value(lane_lse(L, p.heads, s, lane + 64));
+  // Lane k holds the lse of split k and k + 64 with their format bits: the
+  // splits whose rows are wide (many, in peaked inputs) read their (stale)
+  // fp16 slot from one place, the batch's first split, which stays in
+  // cache, instead of from HBM; the choice is an address, not a branch.
+  const float r0 = lane_lse(L, p.heads, s, lane), r1 = lane_lse(L, p.heads, s, lane + 64);
+  const uint64_t wide0 = __builtin_amdgcn_ballot_w64(lse_flag(r0));
+  const uint64_t wide1 = __builtin_amdgcn_ballot_w64(lse_flag(r1));
+  const float l0 = lse_value(r0), l1 = lse_value(r1);
   // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
   // s re-read split s - 1, which then gets weight 0.
   u32x4 v[U];
@@ -1777,7 +1784,8 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
-      v[u] = load_part16x8(p.part16, O + (int64_t)k * stride);
+      const bool wd = k < 64 ? ((wide0 >> k) & 1ull) : k < 128 && ((wide1 >> (k - 64)) & 1ull);
+      v[u] = load_part16x8(p.part16, O + (int64_t)(wd ? k0 : k) * stride);
       lk[u] = L[(int64_t)k * p.heads];
     }
   };

@@ -56,24 +56,33 @@ def workload_figures(lens, heads: int, seqlen_q: int = 1, kv_elt: int = 2):
     return flops, kv_bytes, total_bytes
 
 
+def kernel_code_sha256() -> str:
+    """sha256 of the kernel source with comments and blank lines removed: the
+    fingerprint a counter summary is taken on (a comment edit keeps it)."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
+    text = re.sub(r"/\*.*?\*/", "", open(src).read(), flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    return hashlib.sha256("\n".join(line for line in lines if line.strip()).encode()).hexdigest()
+
+
 def measured_counters(workload: str):
     """From the committed rocprofv3 summary of this workload (profiles/*.md):
     HBM bytes per split-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by a
     plain-copy calibration), the split kernel's MFMA-busy fraction
     (SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES)) and the file.
     None for each when there is no summary for this workload or the kernel
-    source changed since the counters were taken."""
+    code changed since the counters were taken (kernel_code_sha256)."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = kernel_code_sha256()
     traffic = busy = source = None
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(f):
             for tag in ("traffic-json:", "counters-json:"):
                 if line.startswith(tag):
                     rec = json.loads(line.split(":", 1)[1])
-                    if rec.get("workload") != workload or rec.get("source_sha256") != sha:
+                    if rec.get("workload") != workload or rec.get("code_sha256") != sha:
                         continue
                     source = os.path.relpath(f, ROOT)
                     if tag == "traffic-json:":

@@ -6,10 +6,14 @@
 //                    inside split_kernel, every wave for its own work item).
 //   * split_kernel   one workgroup per (work item, head group of 128 heads);
 //                    streams the work item's KV rows through LDS and runs the
-//                    base-2 online softmax with both products on MFMA.
+//                    base-2 online softmax with both products on MFMA.  With
+//                    an FP8 (E4M3) cache the rows arrive as bytes and each
+//                    wave widens its share of a tile to 16 bits in LDS.
 //   * combine_heads_kernel / combine_splitk_kernel merge the per-split
 //                    partials of sequences with s_b > 1: one wave per head for
 //                    few splits, four waves over the splits of a head for many.
+//   * check_block_table_kernel  counts block-table entries a decode would
+//                    read outside the page pool (the split kernel clamps them).
 //
 // What is computed follows the TileLang MLA guide ("用 TileLang 编写高性能
 // DeepSeek MLA 内核"): "Split Kernel" (score tile = q_nope·latentᵀ + q_pe·ropeᵀ

@@ -102,7 +102,8 @@ typedef enum mla_kv_dtype {
  *   kv_latent = pool, k_pe = pool + 512, kv_sb = kpe_sb = page*576,
  *   kv_sr = kpe_sr = 576.  page_block_size must be a positive multiple of 32.
  *   Only entries for j < cache_seqlens[b] are read; other entries may hold
- *   anything (e.g. -1).  Entries that are read must lie in [0, num_pages).
+ *   anything (e.g. -1).  Entries that are read must lie in [0, num_pages);
+ *   one outside is clamped into the pool (see mla_check_block_table).
  *
  * Several query tokens per sequence (speculative / multi-token decode; the
  * FlashMLA analysis's parameter struct carries seqlen_q and is_causal):
@@ -179,7 +180,10 @@ int mla_num_cus(int device, int32_t* num_cus_out /* host */);
 int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32_t* max_work_out /* host */);
 
 /*
- * Bytes of device workspace mla_decode needs for this description:
+ * Bytes of device workspace mla_decode needs for this description.  The
+ * bound is derived here from the split mode and the CU count (a caller
+ * cannot know in advance how many splits the planner will choose), and the
+ * size comes back through bytes_out beside a status, like every call:
  *   plan (int32): B + (B+1) + 4*max_work, rounded to 256 bytes;
  *   partial lse (fp32, base 2): max_work * H, rounded to 256 bytes;
  *   partial rows (fp16, normalised): max_work * H * 512, rounded to 256 bytes;
@@ -190,7 +194,10 @@ int mla_max_work(const mla_desc* desc, int32_t num_split, int32_t num_cus, int32
 int mla_workspace_size(const mla_desc* desc, int32_t num_split, int32_t num_cus, size_t* bytes_out /* host */);
 
 /*
- * Host twin of the planner: same integers as the device planner.
+ * Host twin of the planner: same integers as the device planner.  The plan
+ * comes back in three caller arrays, the layout mla_decode keeps in its
+ * workspace, rather than in one plan struct, so that the two compare
+ * directly.
  *   heads          query rows (as desc->heads); seqlen_q as desc->seqlen_q
  *   cache_seqlens  host int32[batch]
  *   num_splits     host int32[batch]            (out)
@@ -216,9 +223,12 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
  *   kv_latent, k_pe                         cache (see mla_desc)
  *   block_table  int32, NULL for a contiguous cache
  *   cache_seqlens int32[B]; the lengths stay on the device, so they are
- *                  clamped in the kernels rather than checked: a negative
- *                  length counts as 0, and a contiguous cache's lengths are
- *                  capped at desc->max_seqlen
+ *                  clamped in the kernels rather than checked (no status
+ *                  reports them, as none could without a host
+ *                  synchronisation): a negative length counts as 0, and a
+ *                  contiguous cache's lengths are capped at desc->max_seqlen;
+ *                  a paged cache's block_table entries likewise are clamped
+ *                  into the pool (mla_check_block_table finds bad ones)
  *   softmax_scale  multiplies the raw dot products (typically 1/sqrt(576));
  *                  must be finite and > 0 (MLA_ERR_INVALID_ARG otherwise)
  *   num_split  0 = planner chooses s_b per sequence; > 0 forces s_b = num_split

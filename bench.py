@@ -56,18 +56,25 @@ def workload_figures(lens, heads: int, seqlen_q: int = 1, kv_elt: int = 2):
     return flops, kv_bytes, total_bytes
 
 
-def kernel_code_sha256() -> str:
-    """sha256 of the kernel source with comments and blank lines removed: the
-    fingerprint a counter summary is taken on (a comment edit keeps it)."""
+def code_sha256(text: str) -> str:
+    """sha256 of C/HIP source text with comments, trailing blanks and blank
+    lines removed (string literals holding "//" or "/*" are not expected)."""
     import hashlib
     import re
-    src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
-    text = re.sub(r"/\*.*?\*/", "", open(src).read(), flags=re.S)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
     return hashlib.sha256("\n".join(line for line in lines if line.strip()).encode()).hexdigest()
 
 
-def measured_counters(workload: str):
+def kernel_code_sha256() -> str:
+    """code_sha256 of the kernel source: the fingerprint a counter summary is
+    taken on (a comment edit keeps it, a code edit does not)."""
+    src = os.path.join(ROOT, "deepseek_mla_decode_amd", "csrc", "mla_kernels.hip")
+    with open(src) as f:
+        return code_sha256(f.read())
+
+
+def measured_counters(workload: str, profiles_dir: str = os.path.join(ROOT, "profiles"), sha: str = None):
     """From the committed rocprofv3 summary of this workload (profiles/*.md):
     HBM bytes per split-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by a
     plain-copy calibration), the split kernel's MFMA-busy fraction
@@ -75,10 +82,12 @@ def measured_counters(workload: str):
     None for each when there is no summary for this workload or the kernel
     code changed since the counters were taken (kernel_code_sha256)."""
     import glob
-    sha = kernel_code_sha256()
+    sha = sha or kernel_code_sha256()
     traffic = busy = source = None
-    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
-        for line in open(f):
+    for f in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
+        with open(f) as fh:
+            lines = fh.readlines()
+        for line in lines:
             for tag in ("traffic-json:", "counters-json:"):
                 if line.startswith(tag):
                     rec = json.loads(line.split(":", 1)[1])

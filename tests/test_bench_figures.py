@@ -38,3 +38,48 @@ def test_bound_follows_intensity():
     # No launch time: no figures, but the bound is still named.
     first, _ = bench.split_bounds(1.0, 1.0, 0.0, 123)
     assert first["achieved"] is None and first["frac"] is None and first["traffic"] == 123
+
+
+def test_code_hash_ignores_comments_only():
+    src = "int f(int a) {\n  return a + 1;\n}\n"
+    commented = ("// header\n/* block\n   comment */\nint f(int a) {   \n\n"
+                 "  return a + 1;  // trailing\n}\n\n")
+    assert bench.code_sha256(src) == bench.code_sha256(commented)
+    assert bench.code_sha256(src) != bench.code_sha256(src.replace("+ 1", "+ 2"))
+    assert bench.code_sha256(src) != bench.code_sha256(src.replace("  return", "  return 0 *"))
+
+
+def test_measured_counters_follow_the_code_hash(tmp_path):
+    """Counter lines are used for their own workload and only while their code
+    hash is the one asked for."""
+    import json
+    rec = {"workload": "w1", "code_sha256": "abc", "fetch_bytes": 100, "write_bytes": 20}
+    busy = {"workload": "w1", "code_sha256": "abc", "mfma_busy": 0.5}
+    other = {"workload": "w2", "code_sha256": "abc", "fetch_bytes": 7, "write_bytes": 1}
+    (tmp_path / "p.md").write_text("# summary\n"
+                                   f"traffic-json: {json.dumps(rec)}\n"
+                                   f"counters-json: {json.dumps(busy)}\n"
+                                   f"traffic-json: {json.dumps(other)}\n")
+    t, b, src = bench.measured_counters("w1", str(tmp_path), sha="abc")
+    assert t == 120 and b == 0.5 and src.endswith("p.md")
+    assert bench.measured_counters("w1", str(tmp_path), sha="def") == (None, None, None)
+    assert bench.measured_counters("w3", str(tmp_path), sha="abc") == (None, None, None)
+    assert bench.measured_counters("w2", str(tmp_path), sha="abc")[:2] == (8, None)
+
+
+def test_committed_profiles_parse():
+    """Every machine-readable line in profiles/ is JSON with the fields bench.py
+    reads; each workload's counter lines name one code hash."""
+    import glob
+    import json
+    import os
+    seen = {}
+    for f in glob.glob(os.path.join(bench.ROOT, "profiles", "*.md")):
+        for line in open(f):
+            for tag, keys in (("traffic-json:", ("fetch_bytes", "write_bytes")), ("counters-json:", ("mfma_busy",))):
+                if line.startswith(tag):
+                    rec = json.loads(line.split(":", 1)[1])
+                    assert all(k in rec for k in ("workload", "code_sha256") + keys), (f, line)
+                    seen.setdefault(rec["workload"], set()).add(rec["code_sha256"])
+    assert seen, "no counter lines under profiles/"
+    assert all(len(v) == 1 for v in seen.values()), seen

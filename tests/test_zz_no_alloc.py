@@ -35,9 +35,9 @@ def _both(mla, inp, num_split):
     B, H = inp.batch, inp.heads
     out_n = torch.full((B, H, 512), float("nan"), dtype=d["q_nope"].dtype, device="cuda")
     lse_n = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
-    mla.mla_decode_noalloc(*args, num_split=num_split, out=out_n, lse=lse_n)
+    mla.mla_decode_noalloc(*args, num_split=num_split, out=out_n, lse=lse_n, kv_scale=d["kv_scale"])
     torch.cuda.synchronize()
-    out_w, lse_w = mla.mla_decode(*args, num_split=num_split)
+    out_w, lse_w = mla.mla_decode(*args, num_split=num_split, kv_scale=d["kv_scale"])
     torch.cuda.synchronize()
     return (from_device(out_n), from_device(lse_n)), (from_device(out_w), from_device(lse_w))
 
@@ -65,6 +65,16 @@ def test_noalloc_matches_mla_decode_on_two_calls(mla):
     _check(mla, big, 0, "noalloc large, planner")
     small = mi.make_paged(3, 16, [700, 1, 2000], "bf16", seed=162, page_block_size=64, spare_pages=2)
     _check(mla, small, 4, "noalloc small, 4 splits")
+
+
+def test_noalloc_fp8_cache_on_two_calls(mla):
+    """The same entry point over an E4M3 cache: a paged call with the planner,
+    then a smaller contiguous one with forced splits."""
+    lens = np.random.default_rng(163).integers(1, 3000, size=24)
+    big = mi.make_paged(24, 128, lens, "bf16", seed=164, page_block_size=64, spare_pages=3, kv_dtype="fp8")
+    _check(mla, big, 0, "noalloc fp8 paged, planner")
+    small = mi.make_contiguous(2, 32, 400, [400, 57], "f16", seed=165, kv_dtype="fp8")
+    _check(mla, small, 3, "noalloc fp8 small, 3 splits")
 
 
 def test_noalloc_refuses_problems_beyond_the_scratch(mla):

@@ -756,8 +756,8 @@ struct Softmax {
   float dn;             // step 5: c m - c tmax (0 on the first tile)
   u32x4 pk[2], pl[2];   // P packed (bf16: high part in pk, low part in pl)
 
-  // Step `s` (0..22).  `first`: this is the work item's first tile, which
-  // fixes m.
+  // Step `s` (0 .. kSoftmaxSteps<DT> - 1).  `first`: this is the work item's
+  // first tile, which fixes m.
   __device__ __forceinline__ void step(int s, bool first, float c, float& nmc, float& lsum, float& lsr) {
     if (s == 0) { t0 = max3(x[0], x[1], x[2]); t1 = max3(x[3], x[4], x[5]); }
     if (s == 1) { t2 = max3(x[6], x[7], x[8]); t3 = max3(x[9], x[10], x[11]); }
@@ -792,7 +792,15 @@ struct Softmax {
       if constexpr (DT == MLA_DTYPE_F16) {
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         lsr = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), (h2){(_Float16)1.0f, (_Float16)1.0f}, lsr, false);
-      } else {
+      }
+    }
+    // bf16: the low part of pair j, in steps 23..30, which the score MFMAs
+    // of the loop would otherwise pass with only their K reads between them.
+    if constexpr (DT == MLA_DTYPE_BF16) {
+      if (s >= 23 && s < 31) {
+        const int j = s - 23;
+        const uint32_t w = pk[j >> 2][j & 3];
+        const float a = x[2 * j], bb = x[2 * j + 1];
         const float ah = __builtin_bit_cast(float, w << 16);
         const float bh = __builtin_bit_cast(float, w & 0xFFFF0000u);
         pl[j >> 2][j & 3] = pack2<DT>(a - ah, bb - bh);
@@ -800,7 +808,8 @@ struct Softmax {
     }
   }
 };
-constexpr int kSoftmaxSteps = 23;
+template <int DT>
+constexpr int kSoftmaxSteps = DT == MLA_DTYPE_BF16 ? 31 : 23;
 
 // Schedule (one wave, work item of n tiles; tile t in LDS slot t % 4):
 //   prologue   DMA tiles 0, 1, 2; wait for tile 0; barrier
@@ -1252,7 +1261,7 @@ void split_kernel(SplitParams p) {
         if (s + kKA >= kQRegSteps && s + kKA < 36)
           qb[s + kKA - kQRegSteps] = lds_get16(lds_at(xor_add(qwave, 0u, lane16)), (s + kKA - kQRegSteps) * 4096);
         if (with_sm) {
-          if (s < kSoftmaxSteps) sm.step(s, first_prev, c, nmc, lsum, lsr);
+          if (s < kSoftmaxSteps<DT>) sm.step(s, first_prev, c, nmc, lsum, lsr);
           if (s == 30) v_bases(vtile);
           if (s >= 36 - kVA) vbuf[s - (36 - kVA)] = v_read(s - (36 - kVA));
         }
@@ -1388,7 +1397,7 @@ void split_kernel(SplitParams p) {
         sm.x[e] = tile_base + n < lim ? last[e] : -__builtin_inff();
       }
 #pragma unroll
-      for (int s = 0; s < kSoftmaxSteps; ++s) {
+      for (int s = 0; s < kSoftmaxSteps<DT>; ++s) {
         sm.step(s, n_tiles == 1, c, nmc, lsum, lsr);
         if (s == 5) rescale();
       }

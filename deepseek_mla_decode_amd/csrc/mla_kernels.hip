@@ -1763,10 +1763,11 @@ __global__ __launch_bounds__(256) void combine_heads_kernel(CombineParams p) {
 }
 
 // Wave w accumulates splits w, w + 4, ... in batches of kSplitkBatch (8
-// output values per lane; a batch's fp16 partial rows and lse values are
-// read together, the first batch before the final lse is known; the fp32
-// rows of the splits whose lse carries the format bit are added after); the four sums
-// meet in LDS, and wave w writes output columns 128 w .. 128 w + 127.
+// output values per lane), then the four sums meet in LDS and wave w writes
+// output columns 128 w .. 128 w + 127.  A batch's lse values are read one
+// batch ahead, so that each partial row is read in its own format, fp16 or
+// (format bit set) fp32, and a batch costs one memory round trip: its rows
+// go out together with the next batch's lse values.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   __shared__ f32x4 red[4][2][64];   // [wave][half][lane]: 8 values per lane
@@ -1781,50 +1782,59 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(CombineParams p) {
   const float* L = p.part_lse + (int64_t)base * p.heads + h;
   const int64_t stride = (int64_t)p.heads * 512;   // elements between consecutive splits
   const int64_t O = ((int64_t)base * p.heads + h) * 512 + 8 * lane;
-  // Lane k holds the lse of split k and k + 64 with their format bits: the
-  // splits whose rows are wide (many, in peaked inputs) read their (stale)
-  // fp16 slot from one place, the batch's first split, which stays in
-  // cache, instead of from HBM; the choice is an address, not a branch.
-  const float r0 = lane_lse(L, p.heads, s, lane), r1 = lane_lse(L, p.heads, s, lane + 64);
-  const uint64_t wide0 = __builtin_amdgcn_ballot_w64(lse_flag(r0));
-  const uint64_t wide1 = __builtin_amdgcn_ballot_w64(lse_flag(r1));
-  const float l0 = lse_value(r0), l1 = lse_value(r1);
   // Batch of this wave's splits k0, k0 + 4, ..., k0 + 4 (U - 1); indices past
-  // s re-read split s - 1, which then gets weight 0.
-  u32x4 v[U];
-  float lk[U];
-  auto load_batch = [&](int k0) __attribute__((always_inline)) {
+  // s re-read split s - 1 and are left out of the sum.
+  float lk[U], lkn[U];   // the batch's lse values (with format bits), the next batch's
+  auto load_lse = [&](int k0, float* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
-      const bool wd = k < 64 ? ((wide0 >> k) & 1ull) : k < 128 && ((wide1 >> (k - 64)) & 1ull);
-      v[u] = load_part16x8(p.part16, O + (int64_t)(wd ? k0 : k) * stride);
-      lk[u] = L[(int64_t)k * p.heads];
+      dst[u] = L[(int64_t)k * p.heads];
+    }
+  };
+  // Row of split k: 16 bytes of fp16 (va; vb the same again) or 32 bytes of
+  // fp32 (va, vb), chosen by its format bit.
+  u32x4 va[U], vb[U];
+  auto load_rows = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + 4 * u < s ? k0 + 4 * u : s - 1;
+      const int64_t e = O + (int64_t)k * stride;
+      const u32x4* pa = lse_flag(lk[u]) ? reinterpret_cast<const u32x4*>(p.part32 + e)
+                                        : reinterpret_cast<const u32x4*>(p.part16 + e);
+      va[u] = pa[0];
+      vb[u] = pa[lse_flag(lk[u]) ? 1 : 0];
     }
   };
 
-  load_batch(wave);
-  __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the reductions
-  const CombineWeights cw = combine_weights(l0, l1, L, p.heads, s, lane);
+  load_lse(wave, lk);
+  const float l0 = lane_lse(L, p.heads, s, lane), l1 = lane_lse(L, p.heads, s, lane + 64);
+  const CombineWeights cw = combine_weights(lse_value(l0), lse_value(l1), L, p.heads, s, lane);
   const bool any = cw.total != -__builtin_inff();
 
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = wave;;) {
-    auto weight_of = [&](int u) __attribute__((always_inline)) {
-      return any && k0 + 4 * u < s ? __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total) : 0.f;
-    };
-    uint32_t wm = 0;   // lk[u] is the same in every lane
+    load_rows(k0);
+    const int kn = k0 + 4 * U;
+    if (kn < s) load_lse(kn, lkn);
+    __builtin_amdgcn_sched_barrier(0);   // both sets of reads ahead of the sums
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool wd = k0 + 4 * u < s && lse_flag(lk[u]);
-      wm |= wd ? 1u << u : 0u;
-      add_fp16_part(a0, a1, weight_of(u), v[u], wd || k0 + 4 * u >= s);
+      if (!any || k0 + 4 * u >= s) continue;   // uniform: lk[u] is the same in every lane
+      const float w = __builtin_amdgcn_exp2f(lse_value(lk[u]) - cw.total);
+      if (lse_flag(lk[u])) {
+        a0 += w * __builtin_bit_cast(f32x4, va[u]);
+        a1 += w * __builtin_bit_cast(f32x4, vb[u]);
+      } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        a0 += w * __builtin_convertvector(__builtin_bit_cast(h4, u32x2{va[u].x, va[u].y}), f32x4);
+        a1 += w * __builtin_convertvector(__builtin_bit_cast(h4, u32x2{va[u].z, va[u].w}), f32x4);
+      }
     }
-    // Splits k0 + 4 u: the fp32 rows of the wide ones (stride 4 splits).
-    add_fp32_parts<U>(a0, a1, p.part32, O, 4 * stride, k0 * stride, wm, weight_of);
-    k0 += 4 * U;
+    k0 = kn;
     if (k0 >= s) break;
-    load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) lk[u] = lkn[u];
   }
   red[wave][0][lane] = a0;
   red[wave][1][lane] = a1;

@@ -59,8 +59,6 @@
 
 namespace mla {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -74,17 +72,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // ---------------------------------------------------------------------------
 // dtype helpers
 // ---------------------------------------------------------------------------
-
-template <int DT>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (DT == MLA_DTYPE_F16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-}
 
 // MFMAs written as inline asm.  The constraint letter pins the accumulator:
 // "v" for the per-tile score tile, "a" for the P·V accumulator, which owns all
@@ -166,8 +153,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
   }
 }
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Split partials: a row whose values all lie within [-kPart16Max,
 // kPart16Max] is kept in fp16 only; a larger one in fp32 too.  The choice

@@ -141,9 +141,10 @@ def host_cpu():
 
 
 def cpu_baseline(inp, budget_s: float):
-    """Time the fp64 oracle on the first sequences of the workload until ~budget_s.
-    `cores` is the thread count of the BLAS pool the oracle's matrix products
-    run on (the rest of the oracle is single-threaded NumPy)."""
+    """Time the fp64 oracle on the workload's sequences, in order and again from
+    the first, until ~budget_s of work (at least one sequence).  `cores` is the
+    thread count of the BLAS pool the oracle's matrix products run on (the
+    rest of the oracle is single-threaded NumPy)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -152,14 +153,18 @@ def cpu_baseline(inp, budget_s: float):
         threads = 1
     nproc, model = host_cpu()
     done, t0 = 0, time.perf_counter()
-    while done < inp.batch and time.perf_counter() - t0 < budget_s:
-        oracle.mla_decode_ref(inp, batches=[done])
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.mla_decode_ref(inp, batches=[done % inp.batch])
         done += 1
     el = time.perf_counter() - t0
-    flops, _, _ = workload_figures(inp.cache_seqlens[:done], inp.heads, inp.seqlen_q)   # flops only
+    passes, rest = divmod(done, inp.batch)
+    full, _, _ = workload_figures(inp.cache_seqlens, inp.heads, inp.seqlen_q)   # flops only
+    part, _, _ = workload_figures(inp.cache_seqlens[:rest], inp.heads, inp.seqlen_q)
+    flops = passes * full + part
     return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {inp.batch} sequences (all {inp.heads} query rows), fp64 NumPy, "
-                      f"{el:.1f} s wall",
+            "sample": f"{done} sequence decode{'s' if done != 1 else ''} ({passes} passes over all "
+                      f"{inp.batch} sequences + {rest}; "
+                      f"all {inp.heads} query rows each), fp64 NumPy, {el:.1f} s wall",
             "host": {"nproc": nproc, "cpu_model": model}}
 
 
@@ -184,7 +189,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the decode path has no multi-GPU mode", file=sys.stderr)
         return 2
 

@@ -83,3 +83,22 @@ def test_committed_profiles_parse():
                     seen.setdefault(rec["workload"], set()).add(rec["code_sha256"])
     assert seen, "no counter lines under profiles/"
     assert all(len(v) == 1 for v in seen.values()), seen
+
+
+def test_cpu_baseline_cycles_through_the_workload():
+    """The oracle baseline keeps decoding the workload's sequences, from the
+    first again, until its budget is spent, and counts the flops of exactly
+    the sequences it decoded."""
+    import re
+    import mla_inputs as mi
+    inp = mi.make_config(0)   # B=2, H=16, L=256: a few ms per sequence
+    rec = bench.cpu_baseline(inp, 0.3)
+    m = re.match(r"(\d+) sequence decodes? \((\d+) passes over all (\d+) sequences \+ (\d+);", rec["sample"])
+    assert m, rec["sample"]
+    done, passes, batch, rest = map(int, m.groups())
+    assert batch == inp.batch and done == passes * batch + rest and passes >= 1
+    wall = float(re.search(r"([0-9.]+) s wall", rec["sample"]).group(1))
+    full, _, _ = bench.workload_figures(inp.cache_seqlens, inp.heads)
+    part, _, _ = bench.workload_figures(inp.cache_seqlens[:rest], inp.heads)
+    assert np.isclose(rec["value"] * 1e12 * wall, passes * full + part, rtol=0.2)
+    assert rec["kind"] == "oracle" and rec["cores"] >= 1

@@ -734,6 +734,31 @@ def test_wide_partial_rows_over_a_stale_workspace(mla, dtype):
         assert_parity(from_device(o), from_device(l), ro, rl, f"stale workspace {dtype} split={ns}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_wide_and_narrow_rows_past_128_splits(mla, dtype):
+    """More than 128 splits of one block each, 1 % of whole rows x8: the
+    splits holding a scaled row have outputs beyond +-1 (fp32 rows, fp16 slot
+    unwritten), the others stay in fp16, interleaved along the sequence and
+    past the 128 lse values the combine's lanes hold.  The workspace starts
+    as NaN bytes, so a row read in the wrong format shows."""
+    import torch
+    from mla_inputs.torch_io import from_device, to_device
+    lens = [200 * 64, 3000]
+    inp = mi.make_contiguous(len(lens), 32, lens[0], lens, dtype, seed=152)
+    mi.scale_random_rows(inp, 0.01, 8.0, seed=153)
+    d = to_device(inp, "cuda")
+    ro, rl = oracle.mla_decode_ref(inp)
+    cus = mla.mla_num_cus(0)
+    for ns in (150, 200, 0):
+        out = torch.empty((len(lens), 32, 512), dtype=d["q_nope"].dtype, device="cuda")
+        desc = mla.make_desc(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, out)
+        ws = torch.full((mla.mla_workspace_size(desc, ns, cus),), 0xFF, dtype=torch.uint8, device="cuda")
+        o, l = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], None, d["cache_seqlens"],
+                              inp.softmax_scale, num_split=ns, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(from_device(o), from_device(l), ro, rl, f"wide/narrow {dtype} split={ns}")
+
+
 def test_block_table_check_counts_entries_read(mla):
     """mla_check_block_table counts, per sequence, the block-table entries
     mla_decode reads (j < ceil(L / page)) that lie outside the pool; entries

@@ -184,6 +184,10 @@ def main() -> int:
                     help="query heads per token instead of the workload's (e.g. one tensor-parallel shard)")
     ap.add_argument("--seqlen-q", type=int, default=1,
                     help="query tokens per sequence (speculative / multi-token decode), each of H heads")
+    ap.add_argument("--plan-once", action="store_true",
+                    help="make the split plan once (mla_plan_device) and decode with it every step "
+                         "(mla_decode_planned), as a model's layers share one plan per decode step; "
+                         "by default every call plans for itself")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="store the workload's cache as FP8 E4M3 bytes with one scale (workloads 0..3)")
     args = ap.parse_args()
@@ -230,12 +234,21 @@ def main() -> int:
     def tokens(t):   # query rows [B, H, ...] -> [B, S, H / S, ...] when S > 1
         return t if S == 1 else t.view(B, S, H // S, *t.shape[2:])
 
+    # One plan for every copy (their lengths are the same), made before the
+    # timed region when --plan-once asks for it.
+    plan = (mla.mla_plan_device(dev["cache_seqlens"], H, args.num_split, mla.mla_num_cus(), seqlen_q=S)
+            if args.plan_once else None)
+
     def step(i):
         d = devs[i % len(devs)]
-        mla.mla_decode(tokens(d["q_nope"]), tokens(d["q_pe"]), d["kv_latent"], d["k_pe"],
-                       d["block_table"], d["cache_seqlens"], inp.softmax_scale, num_split=args.num_split,
-                       out=tokens(outs[i % len(devs)]), lse=tokens(lses[i % len(devs)]), workspace=ws,
-                       kv_scale=d["kv_scale"])
+        a = (tokens(d["q_nope"]), tokens(d["q_pe"]), d["kv_latent"], d["k_pe"], d["block_table"],
+             d["cache_seqlens"], inp.softmax_scale)
+        kw = dict(num_split=args.num_split, out=tokens(outs[i % len(devs)]), lse=tokens(lses[i % len(devs)]),
+                  workspace=ws, kv_scale=d["kv_scale"])
+        if plan is not None:
+            mla.mla_decode_planned(*a, plan, **kw)
+        else:
+            mla.mla_decode(*a, **kw)
 
     for i in range(args.warmup):
         step(i)
@@ -303,7 +316,8 @@ def main() -> int:
         "config": {"workload": workload, "batch": B, "heads": H // S, "seqlen_q": S,
                    "seqlen_kv_mean": mean_L, "layout": "paged" if inp.paged else "contiguous",
                    "kv_cache": "fp8_e4m3 (one scale)" if kv_elt == 1 else inp.dtype,
-                   "num_split": args.num_split or "planner", "input_copies": len(devs)},
+                   "num_split": args.num_split or "planner", "input_copies": len(devs),
+                   "plan": "made once, reused by every step" if args.plan_once else "in every call"},
         "us_per_call": round(ms * 1e3, 2),
         "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
         "arith_intensity": round(ai, 1),

@@ -26,7 +26,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "mla_decode", "mla_decode_noalloc", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
+    "mla_decode", "mla_decode_noalloc", "mla_decode_planned", "mla_plan_host", "mla_plan_device", "mla_workspace_size", "mla_max_work",
     "mla_num_cus", "mla_last_error", "mla_timing_enable", "mla_timing_read", "make_desc",
     "mla_check_block_table",
     "MlaDesc", "MlaError",
@@ -164,9 +164,24 @@ def mla_decode_noalloc(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens
                       lse, stream=stream, kv_scale=kv_scale, _noalloc=True)
 
 
+def mla_decode_planned(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float, plan,
+                       num_split: int = 0, num_cus: Optional[int] = None, out=None, lse=None, workspace=None,
+                       stream=None, kv_scale: Optional[float] = None) -> Tuple["object", "object"]:
+    """mla_decode with a plan made beforehand: ``plan`` is the ``(num_splits,
+    split_offset, work)`` that ``mla_plan_device(cache_seqlens, heads,
+    num_split, num_cus, seqlen_q=...)`` returned for these lengths; pass the
+    same ``num_split`` and ``num_cus`` (default: this GPU's CU count), which
+    size the workspace.  One plan serves every layer of a decode step; the
+    kernels read the plan and clamp what they read, so a plan made for other
+    lengths gives wrong results, not faults."""
+    return mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out,
+                      lse, workspace, stream, kv_scale, _plan=(plan, num_cus))
+
+
 def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale: float,
                num_split: int = 0, out=None, lse=None, workspace=None,
-               stream=None, kv_scale: Optional[float] = None, _noalloc: bool = False) -> Tuple["object", "object"]:
+               stream=None, kv_scale: Optional[float] = None, _noalloc: bool = False,
+               _plan=None) -> Tuple["object", "object"]:
     """MLA decode through the C ABI; returns ``(out [B,H,512], lse fp32 [B,H])``.
 
     Contiguous cache: ``kv_latent [B, S, 1, 512]``, ``k_pe [B, S, 1, 64]``,
@@ -222,11 +237,26 @@ def mla_decode(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softma
             float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc), s.cuda_stream)
         _lib.check(st)
         return (out4, lse4) if four_d else (out, lse)
+    plan = None
+    if _plan is not None:
+        plan, cus = _plan
+        num_cus = mla_num_cus(q_nope.device.index) if cus is None else int(cus)
+        ns, off, work = _check_plan(plan, B, q_nope)
+    else:
+        num_cus = mla_num_cus(q_nope.device.index)
     if workspace is None:
-        need = mla_workspace_size(desc, num_split, mla_num_cus(q_nope.device.index))
+        need = mla_workspace_size(desc, num_split, num_cus)
         workspace = _workspace(q_nope.device, s.cuda_stream, need)
     elif not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor")
+    if plan is not None:
+        st = _lib.lib().mla_decode_planned(
+            q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(), bt, cache_seqlens.data_ptr(),
+            float(softmax_scale), ns.data_ptr(), off.data_ptr(), work.data_ptr(), int(work.shape[0]),
+            out.data_ptr(), lse.data_ptr(), ctypes.byref(desc), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), s.cuda_stream)
+        _lib.check(st)
+        return (out4, lse4) if four_d else (out, lse)
     st = _lib.lib().mla_decode(
         q_nope.data_ptr(), q_pe.data_ptr(), kv.data_ptr(), kp.data_ptr(), bt, cache_seqlens.data_ptr(),
         float(softmax_scale), int(num_split), out.data_ptr(), lse.data_ptr(), ctypes.byref(desc),
@@ -246,6 +276,24 @@ def _check_placement(q_nope, tensors) -> None:
             continue
         if not t.is_cuda or t.device != q_nope.device:
             raise ValueError(f"{name} is on {t.device}; every tensor must be on q_nope's device {q_nope.device}")
+
+
+def _check_plan(plan, batch: int, q_nope):
+    """(num_splits [B], split_offset [B + 1], work [max_work, 4]): contiguous
+    int32 tensors on q_nope's GPU, as mla_plan_device returns them."""
+    import torch
+    try:
+        ns, off, work = plan
+    except (TypeError, ValueError):
+        raise ValueError("plan must be the (num_splits, split_offset, work) of mla_plan_device") from None
+    _check_placement(q_nope, dict(num_splits=ns, split_offset=off, work=work))
+    for name, t, shape in (("num_splits", ns, (batch,)), ("split_offset", off, (batch + 1,))):
+        if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"plan {name} must be a contiguous int32 tensor of shape {shape}")
+    if work.dtype != torch.int32 or not work.is_contiguous() or work.dim() != 2 or work.shape[1] != 4 \
+            or work.shape[0] < 1:
+        raise ValueError("plan work must be a contiguous int32 tensor [max_work, 4]")
+    return ns, off, work
 
 
 def _check_batch_arrays(batch: int, cache_seqlens, block_table) -> None:

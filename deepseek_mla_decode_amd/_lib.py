@@ -69,6 +69,8 @@ SIGNATURES = {
     "mla_plan_device": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
                                   ctypes.POINTER(MlaDesc), _P, ctypes.c_size_t, _P]),
+    "mla_decode_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I32, _P, _P,
+                                          ctypes.POINTER(MlaDesc), _P, ctypes.c_size_t, _P]),
     "mla_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
                                           ctypes.POINTER(MlaDesc), _P]),
     "mla_check_block_table": (ctypes.c_int, [_P, _P, ctypes.POINTER(MlaDesc), _P, _P]),

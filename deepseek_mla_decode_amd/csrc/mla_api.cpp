@@ -261,16 +261,32 @@ int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, 
   return ok();
 }
 
-// mla_decode and mla_decode_noalloc.  noalloc: the workspace is this
-// device's static scratch array (workspace / workspace_bytes are ignored);
-// nothing here allocates (no events either).
+// A plan made beforehand (mla_decode_planned): device arrays as
+// mla_plan_device writes them, and the capacity they were made with.
+struct GivenPlan {
+  const int32_t* num_splits = nullptr;
+  const int32_t* split_offset = nullptr;
+  const int32_t* work = nullptr;
+  int32_t max_work = 0;
+};
+
+// mla_decode, mla_decode_noalloc and mla_decode_planned.  noalloc: the
+// workspace is this device's static scratch array (workspace /
+// workspace_bytes are ignored); nothing here allocates (no events either).
+// plan: non-null for mla_decode_planned (num_split is 0 then).
 static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
                        const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
                        int32_t num_split, void* out, float* lse, const mla_desc* d, void* workspace,
-                       size_t workspace_bytes, bool noalloc, hipStream_t stream) {
+                       size_t workspace_bytes, bool noalloc, hipStream_t stream, const GivenPlan* plan = nullptr) {
   int st;
   if ((st = check_desc(d)) != MLA_OK) return st;
   if ((st = check_num_split(num_split)) != MLA_OK) return st;
+  if (plan) {
+    if (!plan->num_splits || !plan->split_offset || !plan->work) return fail(MLA_ERR_INVALID_ARG, "NULL plan array");
+    if (plan->max_work < 1) return fail(MLA_ERR_INVALID_ARG, "plan capacity max_work %d < 1", plan->max_work);
+    if (!aligned(plan->num_splits, 4) || !aligned(plan->split_offset, 4) || !aligned(plan->work, 16))
+      return fail(MLA_ERR_INVALID_ARG, "plan arrays must be 4-byte aligned (work 16-byte aligned)");
+  }
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (d->batch == 0) return ok();
@@ -318,7 +334,8 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   int32_t num_cus = 0;
   if ((st = mla_num_cus(device, &num_cus)) != MLA_OK) return st;
   int32_t max_work;
-  if ((st = max_work_of(d, num_split, num_cus, &max_work)) != MLA_OK) return st;
+  if (plan) max_work = plan->max_work;
+  else if ((st = max_work_of(d, num_split, num_cus, &max_work)) != MLA_OK) return st;
   const Layout L = layout(d, max_work);
   if (noalloc) {
     if ((e = mla::noalloc_scratch(&workspace, &workspace_bytes)) != hipSuccess)
@@ -347,9 +364,12 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   sp.kpe = k_pe;
   sp.block_table = block_table;
   sp.seqlens = cache_seqlens;
-  sp.num_splits = num_splits;
-  sp.split_offset = split_offset;
-  sp.work = work;
+  // With a plan made beforehand the kernels read (never write) the caller's
+  // arrays; the workspace's plan region then goes unused.
+  sp.num_splits = plan ? const_cast<int32_t*>(plan->num_splits) : num_splits;
+  sp.split_offset = plan ? const_cast<int32_t*>(plan->split_offset) : split_offset;
+  sp.work = plan ? const_cast<int32_t*>(plan->work) : work;
+
   sp.out = static_cast<uint16_t*>(out);
   sp.lse = lse;
   sp.part16 = part16;
@@ -368,7 +388,7 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   // Forced mode: splits per sequence, the tail included.
   const int32_t seqlen_q = seqlen_q_of(d);
   const int32_t per_seq = num_split > 0 ? num_split + mla::tail_splits(seqlen_q) : 0;
-  sp.num_split = per_seq;
+  sp.num_split = plan ? mla::kPlanGiven : per_seq;
   sp.seqlen_q = seqlen_q;
   sp.heads_per_token = d->heads / seqlen_q;
   sp.batch = d->batch;
@@ -377,7 +397,7 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
   sp.bt_stride = paged ? d->block_table_stride : 0;
   sp.num_pages = paged ? d->num_pages : 0;
   sp.row_cap = row_cap;
-  sp.num_cus = num_cus;
+  sp.num_cus = plan ? max_work : num_cus;
   // An FP8 cache's scale multiplies every score (folded into c) and the
   // output (out_scale); the products use the stored values.
   sp.scale_log2 = kv8 ? (float)((double)softmax_scale * (double)d->kv_scale * 1.4426950408889634)
@@ -396,7 +416,8 @@ static int decode_impl(const void* q_nope, const void* q_pe, const void* kv_late
     cp.part16 = part16;
     cp.part32 = part32;
     cp.part_lse = part_lse;
-    cp.split_offset = split_offset;
+    cp.split_offset = sp.split_offset;
+    cp.max_work = max_work;
     cp.out = static_cast<uint16_t*>(out);
     cp.lse = lse;
     cp.out_sb = d->out_sb;
@@ -429,6 +450,20 @@ int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_late
                        int32_t num_split, void* out, float* lse, const mla_desc* d, hipStream_t stream) {
   return decode_impl(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, num_split, out, lse,
                      d, nullptr, 0, true, stream);
+}
+
+int mla_decode_planned(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                       const int32_t* num_splits, const int32_t* split_offset, const int32_t* work,
+                       int32_t max_work, void* out, float* lse, const mla_desc* d, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  GivenPlan plan;
+  plan.num_splits = num_splits;
+  plan.split_offset = split_offset;
+  plan.work = work;
+  plan.max_work = max_work;
+  return decode_impl(q_nope, q_pe, kv_latent, k_pe, block_table, cache_seqlens, softmax_scale, 0, out, lse, d,
+                     workspace, workspace_bytes, false, stream, &plan);
 }
 
 int mla_check_block_table(const int32_t* block_table, const int32_t* cache_seqlens, const mla_desc* d,

@@ -26,17 +26,23 @@ struct SplitParams {
   int64_t q_nope_sb, q_nope_sh, q_pe_sb, q_pe_sh;
   int64_t kv_sb, kv_sr, kpe_sb, kpe_sr;
   int64_t out_sb, out_sh;
-  int32_t num_split;            // > 0 forced splits per sequence (the tail included), 0 planner mode
+  int32_t num_split;            // > 0 forced splits per sequence (the tail included), 0 planner mode,
+                                // kPlanGiven: num_splits / split_offset / work hold a plan made
+                                // beforehand (read only), num_cus its capacity in work items
   int32_t seqlen_q;             // query tokens per sequence (>= 1)
   int32_t heads_per_token;      // heads / seqlen_q
   int32_t batch, heads;
   int32_t page_size, bt_stride;
   int32_t num_pages;            // paged: page indices are clamped to [0, num_pages)
   int32_t row_cap;              // lengths are clamped to [0, row_cap]
-  int32_t num_cus;              // planner mode: the planner's CU count
+  int32_t num_cus;              // planner mode: the planner's CU count; kPlanGiven: the plan's capacity
   float scale_log2;             // softmax_scale * log2(e) (* kv_scale for an FP8 cache)
   float out_scale;              // FP8 cache: kv_scale (values are decode(byte) * kv_scale); else 1
 };
+
+// SplitParams::num_split of a call with a plan made beforehand (one more
+// field would cost the split kernel scalar registers inside its tile loop).
+constexpr int32_t kPlanGiven = -1;
 
 struct CombineParams {
   const uint16_t* part16;       // [max_work, H, 512] fp16 partial rows
@@ -48,6 +54,7 @@ struct CombineParams {
   int64_t out_sb, out_sh;
   int32_t num_split;
   int32_t heads;
+  int32_t max_work;             // split_offset values are clamped to [0, max_work]
 };
 
 struct PlanParams {

@@ -320,6 +320,26 @@ struct WorkItem {
   bool valid;   // false: past the last work item of the plan
 };
 
+// Work item wi of a plan made beforehand (split_kernel's GIVEN instances;
+// device data, not checked on the host): the work list is in slot order,
+// and num_cus holds the plan's capacity.  Every field is
+// clamped, so that a plan that does not match the lengths gives wrong rows,
+// never an access outside the buffers.
+__device__ __forceinline__ WorkItem given_item(const SplitParams& p, int wi) {
+  WorkItem it{};
+  it.valid = wi < min(p.split_offset[p.batch], p.num_cus);
+  if (!it.valid) return it;
+  const int32_t* w = p.work + 4 * (int64_t)wi;
+  it.b = min(max(w[0], 0), p.batch - 1);
+  const int L = clamp_len(p.seqlens[it.b], p.row_cap);
+  it.s_b = max(p.num_splits[it.b], 1);
+  it.k = min(max(w[1], 0), it.s_b - 1);
+  it.r0 = min(max(w[2], 0), L);
+  it.r1 = min(max(w[3], it.r0), L);
+  it.slot = wi;
+  return it;
+}
+
 // Sequences per lane whose lengths the planner keeps in registers (batch <=
 // 256); larger batches re-read the lengths where they need them.
 constexpr int kPlanRegs = 4;
@@ -809,7 +829,9 @@ constexpr int kSoftmaxSteps = DT == MLA_DTYPE_BF16 ? 31 : 23;
 //   drain      softmax of tile n-1 (masked), P·V of tile n-1.
 // Two tiles stay in flight, one barrier per tile; only the last tile can be
 // partial, so masking is confined to the drain.
-template <int DT, bool PAGED, bool KV8>
+// GIVEN: the work items come from a plan made beforehand (given_item), an
+// instance of its own so that the other instances keep their registers.
+template <int DT, bool PAGED, bool KV8, bool GIVEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitParams p) {
   constexpr int EB = KV8 ? 1 : 2;   // bytes per cache element
@@ -823,7 +845,8 @@ void split_kernel(SplitParams p) {
   // so that the splits of a sequence share one L2 for their queries, and the
   // head groups of a work item its cache rows.
   //
-  // With several query tokens the workgroups come in two kinds,
+  // With several query tokens the workgroups come in two kinds (a plan made
+  // beforehand lists them in slot order and takes the plain bijection),
   // the full-length prefix splits and the one-tile tails (work items below
   // tail * B, see plan_item); each XCD gets an even share of each kind, the
   // prefix splits first, so that the two head groups of a split start
@@ -835,7 +858,7 @@ void split_kernel(SplitParams p) {
     const int total = gridDim.x * ng;
     const int flat = blockIdx.x + blockIdx.y * gridDim.x;
     const int xcd = flat & (kXcds - 1), idx = flat / kXcds;
-    const int nt = tail_splits(p.seqlen_q) * p.batch * ng;   // tail workgroups
+    const int nt = GIVEN ? 0 : tail_splits(p.seqlen_q) * p.batch * ng;   // tail workgroups
     const int nb = total - nt;                                         // the others
     // Workgroups of each kind before XCD x, and on XCD x.
     auto before = [&](int n, int x) { return x * (n / kXcds) + min(x, n % kXcds); };
@@ -879,7 +902,9 @@ void split_kernel(SplitParams p) {
     }
     seq_split_range(clamp_len(p.seqlens[b], p.row_cap), p.seqlen_q, pre, k, &r0, &r1);
   } else {
-    const WorkItem it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
+    WorkItem it;
+    if constexpr (GIVEN) it = given_item(p, wi);
+    else it = plan_item(p, wi, lane, wi == 0 && hg == 0 && wave == 0);
     if (!it.valid) return;   // past the end of the plan
     b = it.b;
     k = it.k;
@@ -1609,8 +1634,8 @@ __device__ __forceinline__ void combine_range(const CombineParams& p, int b, int
     s = p.num_split;
     base = b * p.num_split;
   } else {
-    base = p.split_offset[b];
-    s = p.split_offset[b + 1] - base;
+    base = min(max(p.split_offset[b], 0), p.max_work);
+    s = min(max(p.split_offset[b + 1], base), p.max_work) - base;
   }
 }
 
@@ -2013,8 +2038,14 @@ static void launch_k(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, h
 template <int DT, bool KV8>
 static void launch_split_dt(const SplitParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1) {
-  if (paged) launch_k(split_kernel<DT, true, KV8>, grid, dim3(kThreads), stream, t0, t1, p);
-  else launch_k(split_kernel<DT, false, KV8>, grid, dim3(kThreads), stream, t0, t1, p);
+  const bool given = p.num_split == kPlanGiven;
+  if (paged) {
+    if (given) launch_k(split_kernel<DT, true, KV8, true>, grid, dim3(kThreads), stream, t0, t1, p);
+    else launch_k(split_kernel<DT, true, KV8, false>, grid, dim3(kThreads), stream, t0, t1, p);
+  } else {
+    if (given) launch_k(split_kernel<DT, false, KV8, true>, grid, dim3(kThreads), stream, t0, t1, p);
+    else launch_k(split_kernel<DT, false, KV8, false>, grid, dim3(kThreads), stream, t0, t1, p);
+  }
 }
 
 hipError_t launch_split(const SplitParams& p, int dtype, bool paged, bool kv8, int grid_x, int grid_y,

@@ -211,7 +211,8 @@ int mla_plan_host(const int32_t* cache_seqlens, int32_t batch, int32_t heads, in
 
 /*
  * Device planner: one workgroup reads cache_seqlens (device int32[batch]) and
- * writes num_splits / split_offset / work (device arrays as in mla_plan_host).
+ * writes num_splits / split_offset / work (device arrays as in mla_plan_host),
+ * the plan mla_decode_planned takes.
  */
 int mla_plan_device(const int32_t* cache_seqlens, int32_t batch, int32_t heads, int32_t seqlen_q,
                     int32_t num_split, int32_t num_cus, int32_t* num_splits, int32_t* split_offset, int32_t* work,
@@ -269,6 +270,38 @@ int mla_decode(const void* q_nope, const void* q_pe, const void* kv_latent, cons
 int mla_decode_noalloc(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
                        const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
                        int32_t num_split, void* out, float* lse, const mla_desc* desc, hipStream_t stream);
+
+/*
+ * MLA decode with a plan made beforehand, for callers that decode the same
+ * batch through many layers: one mla_plan_device call per decode step, then
+ * this call per layer, whose split kernel reads its work item from the plan
+ * instead of running the planner rule (FlashMLA's metadata call, whose tile
+ * scheduler metadata and split counts every decode call then takes, plays
+ * the same part: the FlashMLA analysis, "内存访问优化" section).
+ * Arguments as for mla_decode, except:
+ *   num_splits, split_offset, work  device arrays as mla_plan_device wrote
+ *              them (or mla_plan_host's, copied to the device) for this
+ *              call's cache_seqlens, desc->heads, desc->seqlen_q and the
+ *              num_split and num_cus the plan was made with
+ *   max_work   the capacity the plan was made with: mla_max_work(desc,
+ *              num_split, num_cus)
+ *   workspace  at least mla_workspace_size(desc, num_split, num_cus) bytes
+ *              for that same num_split and num_cus (its plan region goes
+ *              unused)
+ * The plan is device data and is not checked against cache_seqlens: every
+ * field the kernels read from it is clamped into range (sequence index,
+ * split index, row range, item count, split offsets), so a plan made for
+ * other lengths gives wrong results, never an access outside the buffers.
+ * With several query tokens the work items run in slot order, not tails
+ * first as in mla_decode (balance across the XCDs only).  Errors as for
+ * mla_decode, plus MLA_ERR_INVALID_ARG for NULL or misaligned plan arrays
+ * and max_work < 1.
+ */
+int mla_decode_planned(const void* q_nope, const void* q_pe, const void* kv_latent, const void* k_pe,
+                       const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                       const int32_t* num_splits, const int32_t* split_offset, const int32_t* work,
+                       int32_t max_work, void* out, float* lse, const mla_desc* desc, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-table check (paged cache).  mla_decode reads block_table entries

@@ -385,3 +385,34 @@ def test_block_table_check_validation(L):
         assert chk(bad_desc) == want, field
         assert L.mla_last_error().decode()
     assert chk(_desc(B=0), bt=None, lens=None, bad=None) == _lib.MLA_OK
+
+
+@pytest.mark.parametrize("case", ["null_num_splits", "null_split_offset", "null_work", "zero_capacity",
+                                  "misaligned_work", "zero_heads"])
+def test_planned_decode_validation(L, case):
+    """mla_decode_planned refuses NULL or misaligned plan arrays and a capacity
+    below one before anything else (no device call); a well-formed call gets
+    past them to the device checks."""
+    d = _desc()
+    ns, off, work, cap = FAKE, FAKE, FAKE, 256
+    if case == "null_num_splits":
+        ns = None
+    elif case == "null_split_offset":
+        off = None
+    elif case == "null_work":
+        work = None
+    elif case == "zero_capacity":
+        cap = 0
+    elif case == "misaligned_work":
+        work = FAKE + 4
+    elif case == "zero_heads":
+        d.heads = 0
+
+    def call(desc, ns, off, work, cap, ws=FAKE, ws_bytes=1 << 40):
+        return L.mla_decode_planned(FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.c_float(1 / 24), ns, off, work,
+                                    cap, FAKE, FAKE, ctypes.byref(desc), ws, ws_bytes, None)
+
+    st = call(d, ns, off, work, cap)
+    assert st == _lib.MLA_ERR_INVALID_ARG, (case, st, L.mla_last_error())
+    assert L.mla_last_error().decode()
+    assert call(_desc(), FAKE, FAKE, FAKE, 256, ws=None, ws_bytes=0) in (_lib.MLA_ERR_WORKSPACE, _lib.MLA_ERR_HIP)

@@ -30,7 +30,7 @@ def asm(tmp_path_factory):
 
 def test_split_kernels_have_no_mfma_result_hazards(asm):
     found = asm_hazards.kernel_hazards(asm, "split_kernel")
-    assert len(found) == 8, sorted(found)
+    assert len(found) == 16, sorted(found)
     bad = {k: v[:5] for k, v in found.items() if v}
     assert not bad, bad
 
@@ -69,7 +69,7 @@ def _loop_bodies(asm, kernel):
 
 def test_tile_loops_do_not_touch_scratch(asm):
     kernels = sorted(set(re.findall(r"^(_ZN3mla12split_kernel\w+):", asm, flags=re.M)))
-    assert len(kernels) == 8
+    assert len(kernels) == 16
     for k in kernels:
         loops = [b for b in _loop_bodies(asm, k) if sum("v_mfma" in y for y in b) >= 64]
         assert loops, f"{k}: tile loop not found"

@@ -65,10 +65,11 @@ def test_paged(mla, page, dtype):
         assert_parity(out, lse, ro, rl, f"fp8 paged page={page} {dtype} split={ns}")
 
 
-@pytest.mark.parametrize("heads", [1, 16, 33, 96, 160])
+@pytest.mark.parametrize("heads", [1, 16, 33, 96, 160, 256])
 def test_head_counts(mla, heads):
     """Fewer heads than a group: waves with no heads only load and widen their
-    share of every tile."""
+    share of every tile; 160 and 256 heads take two head groups, each widening
+    the same tiles in a workgroup of its own."""
     inp = mi.make_contiguous(3, heads, 150, [150, 77, 5], "f16", seed=202, kv_dtype="fp8")
     for ns in (0, 2):
         out, lse = _run(mla, inp, ns)
@@ -156,6 +157,10 @@ def test_bad_scales_are_rejected(mla):
 def test_full_b64_l4096_f16_kvfp8(mla):
     """The headline shape with an FP8 cache: every sequence and head."""
     _full_inputs(mla, mi.make_config(1, kv_dtype="fp8"), (0, 1), "b64_h128_l4096_f16_kvfp8")
+
+
+def test_full_b128_l8192_f16_kvfp8(mla):
+    _full_inputs(mla, mi.make_config(2, kv_dtype="fp8"), (0,), "b128_h128_l8192_f16_kvfp8")
 
 
 def test_full_paged_variable_bf16_kvfp8(mla):

@@ -3,7 +3,9 @@
 // Kernels:
 //   * plan_kernel    one workgroup; turns cache_seqlens into the split plan
 //                    (the stand-alone planner entry point; decode itself plans
-//                    inside split_kernel, every wave for its own work item).
+//                    inside split_kernel, every wave for its own work item, or
+//                    reads its item from a plan made beforehand: the GIVEN
+//                    instances).
 //   * split_kernel   one workgroup per (work item, head group of 128 heads);
 //                    streams the work item's KV rows through LDS and runs the
 //                    base-2 online softmax with both products on MFMA.  With
@@ -32,7 +34,8 @@
 //     l % 32 and half g = l / 32 of the contraction slots of every MFMA.
 //   * Scores are formed transposed, Sᵀ[n][h] = K[n][:]·Q[h][:], with
 //     v_mfma_f32_32x32x16: A = 32 cache rows × 16 dims read from LDS, B = the
-//     wave's Q slice held in 144 VGPRs for the whole work item.  Each lane then
+//     wave's Q slice: its 512 latent dims in 128 VGPRs for the whole work
+//     item, its 64 RoPE dims in LDS.  Each lane then
 //     holds 16 scores of ONE head, so max/sum need a single cross-lane step
 //     (lane l ^ 32) and P is already laid out as the B operand of P·V.
 //   * Output is also transposed, Oᵀ[v][h] += Vᵀ[v][n]·Pᵀ[n][h]: 16 MFMA tiles

@@ -213,7 +213,15 @@ def pin_split_invariance(orc):
 
 
 def pin_split_ranges(orc):
-    """Ranges cover [0, L) once, in order, with sizes differing by at most one block."""
+    """Ranges cover [0, L) once, in order, with sizes differing by at most one
+    block; and three cases worked by hand from the rule (nb = ceil(L / 64)
+    blocks, split k takes floor(nb / s) of them plus one while k < nb mod s):
+    L = 300, s = 2 has 5 blocks, 3 then 2; L = 65, s = 3 has 2 blocks, one
+    each for the first two splits and none for the third; L = 4096, s = 4
+    gives 16 blocks to each."""
+    assert orc.split_ranges(300, 2) == [(0, 192), (192, 300)]
+    assert orc.split_ranges(65, 3) == [(0, 64), (64, 65), (65, 65)]
+    assert orc.split_ranges(4096, 4) == [(0, 1024), (1024, 2048), (2048, 3072), (3072, 4096)]
     for L in (0, 1, 63, 64, 65, 300, 4096, 131072):
         for s in (1, 2, 3, 4, 7, 64, 128):
             r = orc.split_ranges(L, s)

@@ -41,6 +41,10 @@ MUTANTS = {
     "fp8_subnormal": ("m / 8.0 * 2.0 ** -6", "m / 8.0 * 2.0 ** -7"),
     "fp8_mantissa": ("(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),
     "fp8_no_scale": ('return rows * kv_scale if dtype == "fp8" else rows', "return rows"),
+    "fp8_sign_bit": ("np.where(b & 0x80, -1.0, 1.0)", "np.where(b & 0x40, -1.0, 1.0)"),
+    "fp8_nan_finite": ("mag = np.where((e == 15) & (b & 0x7 == 7), np.nan, mag)", "mag = mag"),
+    "fp8_exponent_field": ("e = (b >> 3) & 0xF", "e = (b >> 4) & 0xF"),
+    "split_block_rows": ("SPLIT_BLOCK_ROWS = 64", "SPLIT_BLOCK_ROWS = 32"),
 }
 
 

@@ -22,7 +22,9 @@
  *
  * Conventions for every entry point
  *   - Device pointers are plain HIP device addresses; host pointers are marked.
- *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - The caller owns every buffer.  No call allocates device memory; the
+ *     one static array the library holds (mla_decode_noalloc's scratch) is
+ *     created with the code when the library loads on a GPU.
  *   - Work is enqueued on `stream` only; no call synchronises the device.
  *     Inputs must stay alive until the stream reaches the call.
  *   - Return value: MLA_OK (0) or a negative mla_status.  On an argument error

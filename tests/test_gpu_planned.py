@@ -53,7 +53,8 @@ def _both(mla, inp, num_split):
     return (op, lp), (od, ld)
 
 
-@pytest.mark.parametrize("case", ["contiguous_f16", "paged_bf16_varlen", "forced_5", "kv_fp8", "two_tokens"])
+@pytest.mark.parametrize("case", ["contiguous_f16", "paged_bf16_varlen", "forced_5", "kv_fp8", "two_tokens",
+                                  "forced_3_four_tokens", "two_head_groups"])
 def test_planned_matches_mla_decode_bitwise(mla, case):
     import torch
     from mla_inputs.torch_io import from_device
@@ -68,8 +69,14 @@ def test_planned_matches_mla_decode_bitwise(mla, case):
     elif case == "kv_fp8":
         inp = mi.make_contiguous(8, 128, 2000, [2000, 1, 33, 700, 1999, 64, 65, 1000], "f16", seed=302,
                                  kv_dtype="fp8")
-    else:
+    elif case == "two_tokens":
         inp = mi.make_paged(5, 64, [3, 64, 65, 700, 2500], "f16", seed=303, page_block_size=64, seqlen_q=2)
+    elif case == "forced_3_four_tokens":
+        # forced prefix splits plus the two tail splits per sequence in the plan
+        inp = mi.make_paged(4, 128, [4, 40, 333, 1500], "bf16", seed=304, page_block_size=64, seqlen_q=4)
+        num_split = 3
+    else:
+        inp = mi.make_contiguous(3, 256, 900, [900, 17, 450], "bf16", seed=305)
     (op, lp), (od, ld) = _both(mla, inp, num_split)
     assert torch.equal(op, od), f"{case}: planned output differs from mla_decode's"
     assert torch.equal(torch.nan_to_num(lp), torch.nan_to_num(ld)) and torch.equal(torch.isneginf(lp),

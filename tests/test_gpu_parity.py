@@ -759,6 +759,32 @@ def test_wide_and_narrow_rows_past_128_splits(mla, dtype):
         assert_parity(from_device(o), from_device(l), ro, rl, f"wide/narrow {dtype} split={ns}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_combine_large_batches(mla, dtype):
+    """Batches larger than the GPU's CUs: forced two splits over 130 sequences,
+    some of them empty (the combine's one-wave-per-head grid then runs in more
+    than one round of waves); and planner mode with one long sequence among
+    199 short ones, where the short ones take one split each (their split
+    writes the output) and the long one takes many; with 97 heads the
+    group's last wave has a single head."""
+    cus = mla.mla_num_cus(0)
+    lens = [20000] + list(np.random.default_rng(170).integers(1, 400, size=199))
+    lens[5] = 0
+    inp = mi.make_paged(len(lens), 97, lens, dtype, seed=171, page_block_size=64)
+    ns_arr, _, _ = mla.mla_plan_host(np.asarray(lens, np.int32), 97, 0, cus)
+    assert int(ns_arr[0]) > 2 and int(np.max(ns_arr[1:])) <= 2
+    out, lse = _run(mla, inp, 0)
+    ro, rl = oracle.mla_decode_ref(inp)
+    assert_parity(out, lse, ro, rl, f"large batch planner {dtype}")
+    assert (out[5] == 0).all() and np.isneginf(lse[5]).all()
+    lens2 = list(np.random.default_rng(172).integers(0, 900, size=130))
+    lens2[7] = lens2[8] = 0
+    inp2 = mi.make_contiguous(130, 128, 900, lens2, dtype, seed=173)
+    out, lse = _run(mla, inp2, 2)
+    ro, rl = oracle.mla_decode_ref(inp2)
+    assert_parity(out, lse, ro, rl, f"large batch forced {dtype}")
+
+
 def test_block_table_check_counts_entries_read(mla):
     """mla_check_block_table counts, per sequence, the block-table entries
     mla_decode reads (j < ceil(L / page)) that lie outside the pool; entries

@@ -54,7 +54,8 @@ def _both(mla, inp, num_split):
 
 
 @pytest.mark.parametrize("case", ["contiguous_f16", "paged_bf16_varlen", "forced_5", "kv_fp8", "two_tokens",
-                                  "forced_3_four_tokens", "two_head_groups"])
+                                  "forced_3_four_tokens", "two_head_groups", "kv_fp8_paged_f16",
+                                  "kv_fp8_paged_bf16_two_tokens", "kv_fp8_contiguous_bf16"])
 def test_planned_matches_mla_decode_bitwise(mla, case):
     import torch
     from mla_inputs.torch_io import from_device
@@ -75,8 +76,16 @@ def test_planned_matches_mla_decode_bitwise(mla, case):
         # forced prefix splits plus the two tail splits per sequence in the plan
         inp = mi.make_paged(4, 128, [4, 40, 333, 1500], "bf16", seed=304, page_block_size=64, seqlen_q=4)
         num_split = 3
-    else:
+    elif case == "two_head_groups":
         inp = mi.make_contiguous(3, 256, 900, [900, 17, 450], "bf16", seed=305)
+    elif case == "kv_fp8_paged_f16":
+        inp = mi.make_paged(6, 128, [1, 64, 65, 1500, 0, 3100], "f16", seed=306, page_block_size=64,
+                            kv_dtype="fp8")
+    elif case == "kv_fp8_paged_bf16_two_tokens":
+        inp = mi.make_paged(5, 64, [2, 33, 640, 2047, 2500], "bf16", seed=307, page_block_size=128, seqlen_q=2,
+                            kv_dtype="fp8")
+    else:
+        inp = mi.make_contiguous(4, 128, 1800, [1800, 1, 900, 95], "bf16", seed=308, kv_dtype="fp8")
     (op, lp), (od, ld) = _both(mla, inp, num_split)
     assert torch.equal(op, od), f"{case}: planned output differs from mla_decode's"
     assert torch.equal(torch.nan_to_num(lp), torch.nan_to_num(ld)) and torch.equal(torch.isneginf(lp),

@@ -45,6 +45,9 @@ MUTANTS = {
     "fp8_nan_finite": ("mag = np.where((e == 15) & (b & 0x7 == 7), np.nan, mag)", "mag = mag"),
     "fp8_exponent_field": ("e = (b >> 3) & 0xF", "e = (b >> 4) & 0xF"),
     "split_block_rows": ("SPLIT_BLOCK_ROWS = 64", "SPLIT_BLOCK_ROWS = 32"),
+    "empty_lse_zero": ("        return np.full(H, -np.inf)", "        return np.zeros(H)"),
+    "empty_out_nonzero": ("    out[empty] = 0.0\n", "    out[empty] = 1.0\n"),
+    "combine_weight_base": ("w = np.exp2(lses - total)", "w = np.exp(lses - total)"),
 }
 
 

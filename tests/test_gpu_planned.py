@@ -171,3 +171,59 @@ def test_planned_argument_errors(mla):
     st = L.mla_decode_planned(*common, ns.data_ptr(), off.data_ptr(), work.data_ptr(), 0, *tail)
     assert st == mla._lib.MLA_ERR_INVALID_ARG and "max_work" in mla.mla_last_error()
     torch.cuda.synchronize()
+
+
+def test_graph_of_plan_and_layers_follows_new_lengths(mla):
+    """A decode step as a serving loop captures it: the plan (mla_plan_device)
+    and two layers' planned decodes in one HIP graph, replayed after the
+    lengths tensor has been rewritten in place (a step that appended a token
+    to every sequence, then back).  The plan is made inside the graph, so each
+    replay follows the current lengths: every layer's output equals an eager
+    mla_decode call on the same lengths bit for bit, and the longer step
+    matches the oracle."""
+    import torch
+    from mla_inputs.torch_io import to_device, from_device
+    lens1 = [700, 1, 2000, 64, 0, 1500]
+    lens2 = [701, 2, 2001, 65, 1, 1501]
+    inps = [mi.make_paged(6, 128, lens2, "bf16", seed=340 + i, page_block_size=64) for i in range(2)]
+    layers = [to_device(inp, "cuda") for inp in inps]
+    cus = mla.mla_num_cus(0)
+    seqlens = torch.tensor(lens1, dtype=torch.int32, device="cuda")
+    outs = [torch.empty((6, 128, 512), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    lses = [torch.empty((6, 128), dtype=torch.float32, device="cuda") for _ in layers]
+    d0 = layers[0]
+    desc = mla.make_desc(d0["q_nope"], d0["q_pe"], d0["kv_latent"], d0["k_pe"], d0["block_table"], outs[0])
+    ws = torch.empty(mla.mla_workspace_size(desc, 0, cus), dtype=torch.uint8, device="cuda")
+    scale = inps[0].softmax_scale
+
+    def step():
+        plan = mla.mla_plan_device(seqlens, 128, 0, cus)
+        for d, o, l in zip(layers, outs, lses):
+            mla.mla_decode_planned(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], seqlens,
+                                   scale, plan, num_cus=cus, out=o, lse=l, workspace=ws)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.synchronize()
+    for r, lens in enumerate((lens2, lens1, lens2)):
+        seqlens.copy_(torch.tensor(lens, dtype=torch.int32))
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (d, o, l) in enumerate(zip(layers, outs, lses)):
+            eo, el = mla.mla_decode(d["q_nope"], d["q_pe"], d["kv_latent"], d["k_pe"], d["block_table"], seqlens,
+                                    scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, eo), f"replay {r} layer {i}: output differs from eager"
+            assert torch.equal(torch.nan_to_num(l), torch.nan_to_num(el)) and torch.equal(
+                torch.isneginf(l), torch.isneginf(el)), f"replay {r} layer {i}: lse differs from eager"
+    ro, rl = oracle.mla_decode_ref(inps[1])
+    assert_parity(from_device(outs[1]), from_device(lses[1]), ro, rl, "graph replay, longer step")
